@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for exact attention, shared by the oracle tests, the GPU
+parity tests and the bench.
+
+This module holds no attention arithmetic. It only draws random numbers, rounds them
+to bfloat16 bit patterns, and builds the masks' *inputs* (key-padding lengths, the
+128x128 block table). Everything the method computes lives elsewhere: the fp64 oracle
+under ``oracle/`` and the HIP kernels under ``csrc/``. Both read the same bf16 bits.
+
+Workload shapes follow the pages' training workloads only by shape (BERT-large-like,
+GPT-2-small-like, long causal, block-sparse); no dataset is read.
+
+Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
+  1. draw Q, K, V, dO in that order with ``standard_normal(dtype=float32)``,
+     C-order ``[B][H][N][d]``;
+  2. round each float32 to bf16 with round-to-nearest-even on the bit pattern;
+  3. then, if the workload has one, draw the mask input:
+     key padding: ``integers(128, 513, size=B)`` (valid length per sequence);
+     block mask:  all diagonal blocks kept, plus a uniform draw without replacement
+     of off-diagonal blocks until the kept fraction is ``density``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+BLOCK = 128  # block-mask granularity in both query and key directions
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and return the
+    16-bit patterns as uint16. Inputs must be finite (true for every generator here)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32 (used by generators and tests to
+    look at inputs; both compute paths do their own widening)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool = False
+    mask: str = "none"          # "none" | "kpad" | "block"
+    density: float = 1.0        # kept fraction of 128x128 blocks for mask == "block"
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to float32 (the value both sides receive)."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def with_n(self, n: int) -> "Workload":
+        return dataclasses.replace(self, N=n, name=f"{self.name}_N{n}")
+
+
+# The five workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer,
+# a BERT-large-shaped padded layer, a long causal head set, and a block-sparse layer.
+WORKLOADS = {
+    "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
+    "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
+    "bertl_kpad_512": Workload("bertl_kpad_512", 16, 16, 512, 64, mask="kpad", seed=46003),
+    "long_causal_16k": Workload("long_causal_16k", 1, 16, 16384, 128, causal=True, seed=46004),
+    "blocksparse_8k": Workload("blocksparse_8k", 2, 8, 8192, 64, mask="block", density=0.25,
+                               seed=46005),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """bf16 bit patterns (uint16, [B][H][N][d]) plus optional mask inputs."""
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    kv_len: np.ndarray | None = None      # int32 [B]
+    blockmask: np.ndarray | None = None   # uint8 [nb][nb], nb = ceil(N/128)
+
+
+def n_blocks(n: int) -> int:
+    return (n + BLOCK - 1) // BLOCK
+
+
+def draw_block_mask(rng: np.random.Generator, n: int, density: float) -> np.ndarray:
+    """Diagonal blocks always kept, plus off-diagonal blocks drawn uniformly without
+    replacement until round(density * nb^2) blocks are kept in total."""
+    nb = n_blocks(n)
+    total = int(round(density * nb * nb))
+    extra = max(0, total - nb)
+    off = np.array([r * nb + c for r in range(nb) for c in range(nb) if r != c], dtype=np.int64)
+    mask = np.eye(nb, dtype=np.uint8)
+    if extra:
+        pick = rng.choice(off.size, size=extra, replace=False)
+        mask.reshape(-1)[off[pick]] = 1
+    return mask
+
+
+def make_inputs(wl: Workload, need_do: bool = True) -> Inputs:
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    shape = (wl.B, wl.H, wl.N, wl.d)
+    q = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    do = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)) if need_do else None
+    kv_len = None
+    blockmask = None
+    if wl.mask == "kpad":
+        kv_len = rng.integers(128, 513, size=wl.B).astype(np.int32)
+        kv_len = np.minimum(kv_len, wl.N).astype(np.int32)
+    elif wl.mask == "block":
+        blockmask = draw_block_mask(rng, wl.N, wl.density)
+    return Inputs(wl, q, k, v, do, kv_len, blockmask)
+
+
+def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal") -> tuple:
+    """Small ad-hoc shapes for edge-case tests: returns (q, k, v, do) bf16 bits.
+    ``dist="normal"`` draws N(0,1); ``"wide"`` draws N(0, 3^2) to stress the softmax."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    sd = 3.0 if dist == "wide" else 1.0
+    out = []
+    for _ in range(4):
+        out.append(f32_to_bf16_bits((sd * rng.standard_normal(shape)).astype(np.float32)))
+    return tuple(out)

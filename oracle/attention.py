@@ -1,0 +1,230 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY. This module is imported by ``tests/``, by the package's
+``smoke()`` check and by the bench's CPU-baseline leg; the library under
+``exact_io_aware_46_amd/`` never imports, links or calls it, and it shares no code with
+the HIP path (its bf16 widening, masking, softmax and gradients are written here).
+
+What it computes is the plain definition, materialised: the score matrix S and the
+probability matrix P are formed in full (per head, per panel of query rows), in float64.
+
+* Standard attention S = Q K^T, P = softmax(S), O = P V, with a mask applied to the
+  scores for GPT-style models -- "FlashAttention学习笔记" (amentiraz.github.io),
+  section Forward运作流程 / 标准attention计算.
+* The softmax is the safe one (row maximum subtracted before exponentiating) -- same
+  page, section 标准Safe softmax.
+* Order of operations: matmul, scaling, masking, softmax, multiplication by V --
+  "高效注意力算法实现 (FlashAttention)" (apxml.com), section FlashAttention：融合算子与
+  分块处理 (kernel fusion bullet). FlashAttention returns exactly this output (same page,
+  same section, and 优势与影响: exactness).
+* The saved softmax statistic used by backward recomputation -- report on
+  "FlashAttention：一种基于I/O感知的快速且内存高效的自注意力算法" (fmread.com), section
+  算法设计 (backward bullet). Read here as one log-sum-exp per row, natural log.
+* Block-sparse attention (same report, 研究亮点 item 3; and the abstract of
+  "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness",
+  aha.fim.ai) is read as: a 128x128 table over (query block, key block), nonzero = the
+  block's scores are kept, zero = they are masked to -inf.
+
+Readings where the pages are silent (each one is listed with its reasons in the design
+notes of the repository):
+* scale multiplies Q K^T before masking; the float32 scale is widened exactly;
+* causal means key j is allowed for query i iff j <= i (equal lengths);
+* key padding (valid length L_b per batch entry) masks keys j >= L_b for every query;
+* the three masks compose by logical AND;
+* a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
+* backward is the derivative of the scalar L = sum(dO * O) with respect to Q, K, V:
+  dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic, dS = P * (dP - D),
+  dQ = scale * dS K, dK = scale * dS^T Q  (textbook softmax calculus; the pages say
+  only that backward recomputes P from the saved statistic).
+
+Row panels: to bound memory at long N the query rows of a head are processed in panels.
+Every row-local quantity (S row, LSE, P row, O row, D_i, dP row, dS row, dQ row) is
+identical to the whole-matrix computation; dK and dV are sums over rows and are
+accumulated panel by panel in float64 (only the fp64 summation order differs).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK_BLOCK = 128
+DEFAULT_PANEL = 4096
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Accept either bf16 bit patterns (uint16) or real arrays."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return widen_bf16(x)
+    return x.astype(np.float64)
+
+
+def allowed(rows: np.ndarray, n_keys: int, causal: bool, blockmask, kv_len_b) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend to key j."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    i = rows[:, None]
+    ok = np.ones((rows.size, n_keys), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if blockmask is not None:
+        bm = np.asarray(blockmask) != 0
+        ok &= bm[i // MASK_BLOCK, j // MASK_BLOCK]
+    if kv_len_b is not None:
+        ok &= j < int(kv_len_b)
+    return ok
+
+
+def _scores(Qr, K, s, ok):
+    """S = s * Q K^T on the given query rows, -inf where not allowed."""
+    S = s * (Qr @ K.T)
+    S[~ok] = -np.inf
+    return S
+
+
+def _logsumexp_rows(S):
+    """Safe log-sum-exp of each row; -inf for a row with no finite entry."""
+    m = S.max(axis=1)
+    lse = np.full(m.shape, -np.inf)
+    live = np.isfinite(m)
+    if live.any():
+        Sl = S[live]
+        lse[live] = m[live] + np.log(np.exp(Sl - m[live][:, None]).sum(axis=1))
+    return lse
+
+
+def _probs(S, lse):
+    """P = exp(S - LSE) row by row; rows with LSE = -inf are all zero."""
+    P = np.zeros_like(S)
+    live = np.isfinite(lse)
+    if live.any():
+        P[live] = np.exp(S[live] - lse[live][:, None])
+    return P
+
+
+def _scale64(scale: float) -> float:
+    return float(np.float32(scale))
+
+
+def _head_view(x, b, h):
+    return as_f64(x[b, h])
+
+
+def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
+                 rows=None, panel=DEFAULT_PANEL):
+    """One head: returns (O[rows], LSE[rows]) in float64."""
+    N = Kh.shape[0]
+    s = _scale64(scale)
+    rows = np.arange(Qh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.zeros((rows.size, Vh.shape[1]))
+    LSE = np.zeros(rows.size)
+    for r0 in range(0, rows.size, panel):
+        rr = rows[r0:r0 + panel]
+        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b))
+        lse = _logsumexp_rows(S)
+        P = _probs(S, lse)
+        O[r0:r0 + rr.size] = P @ Vh
+        LSE[r0:r0 + rr.size] = lse
+    return O, LSE
+
+
+def head_backward(Qh, Kh, Vh, dOh, scale, causal=False, blockmask=None, kv_len_b=None,
+                  panel=DEFAULT_PANEL):
+    """One head, all rows: returns dict with O, LSE, D, dQ, dK, dV (float64)."""
+    N, d = Kh.shape
+    s = _scale64(scale)
+    out = {k: np.zeros((N, d)) for k in ("O", "dQ", "dK", "dV")}
+    out["LSE"] = np.zeros(N)
+    out["D"] = np.zeros(N)
+    for r0 in range(0, N, panel):
+        rr = np.arange(r0, min(N, r0 + panel))
+        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b))
+        lse = _logsumexp_rows(S)
+        P = _probs(S, lse)
+        O = P @ Vh
+        dO = dOh[rr]
+        D = (dO * O).sum(axis=1)
+        dP = dO @ Vh.T
+        dS = P * (dP - D[:, None])
+        out["O"][rr] = O
+        out["LSE"][rr] = lse
+        out["D"][rr] = D
+        out["dQ"][rr] = s * (dS @ Kh)
+        out["dK"] += s * (dS.T @ Qh[rr])
+        out["dV"] += P.T @ dO
+    return out
+
+
+def _kv_len_b(kv_len, b):
+    return None if kv_len is None else int(np.asarray(kv_len)[b])
+
+
+def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None):
+    """All heads. q, k, v: [B][H][N][d] (bf16 bits or reals). Returns O, LSE (float64)."""
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    LSE = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], LSE[b, h] = head_forward(_head_view(q, b, h), _head_view(k, b, h),
+                                              _head_view(v, b, h), scale, causal, blockmask,
+                                              _kv_len_b(kv_len, b))
+    return O, LSE
+
+
+def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None):
+    """All heads. Returns dict of float64 arrays: O, LSE, D, dQ, dK, dV."""
+    B, H, N, d = q.shape
+    res = {key: np.zeros((B, H, N, d)) for key in ("O", "dQ", "dK", "dV")}
+    res["LSE"] = np.zeros((B, H, N))
+    res["D"] = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            r = head_backward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
+                              _head_view(do, b, h), scale, causal, blockmask,
+                              _kv_len_b(kv_len, b))
+            for key in res:
+                res[key][b, h] = r[key]
+    return res
+
+
+def forward_rows(q, k, v, scale, sel, causal=False, blockmask=None, kv_len=None):
+    """Sampled rows: ``sel`` is a sequence of (b, h, i). Returns O [len, d], LSE [len]."""
+    d = q.shape[3]
+    O = np.zeros((len(sel), d))
+    LSE = np.zeros(len(sel))
+    for n, (b, h, i) in enumerate(sel):
+        o, l = head_forward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
+                            scale, causal, blockmask, _kv_len_b(kv_len, b), rows=[i])
+        O[n], LSE[n] = o[0], l[0]
+    return O, LSE
+
+
+def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None):
+    """Sampled dQ rows (each row of dQ depends only on its own row of P and dP)."""
+    N, d = q.shape[2], q.shape[3]
+    s = _scale64(scale)
+    out = np.zeros((len(sel), d))
+    for n, (b, h, i) in enumerate(sel):
+        Qh, Kh, Vh = _head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h)
+        dOi = as_f64(do[b, h, i])[None, :]
+        S = _scores(Qh[[i]], Kh, s, allowed([i], N, causal, blockmask, _kv_len_b(kv_len, b)))
+        lse = _logsumexp_rows(S)
+        P = _probs(S, lse)
+        O = P @ Vh
+        D = (dOi * O).sum(axis=1)
+        dP = dOi @ Vh.T
+        dS = P * (dP - D[:, None])
+        out[n] = (s * (dS @ Kh))[0]
+    return out
+
+
+def delta(o, do):
+    """D = rowsum(dO * O) over the given arrays (e.g. the bf16 O a kernel wrote)."""
+    return (as_f64(o) * as_f64(do)).sum(axis=-1)
+

@@ -1,0 +1,400 @@
+"""Pins for the fp64 oracle: each test ties it to something other than itself.
+
+* brute force: per-element Python loops with math.fsum / math.exp on tiny shapes,
+  including shapes past one 128-wide mask block;
+* a library routine: torch CPU float64 softmax attention and autograd gradients;
+* closed forms: hand-derived 2x2 example (tests/golden), N = 1, constant V, causal
+  row 0, causal with Q = 0 (prefix means, LSE = ln(i+1));
+* invariants: rows of P sum to 1 (read through V = I), shift invariance along keys,
+  D computed two ways, mask identities (full length == no padding, all-ones block
+  table == dense, diagonal block table == independent 128-chunks);
+* central finite differences of L = sum(dO * O) for the gradients;
+* planted mistakes: perturbed copies of the backward must fail the pins above.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, sd=1.0):
+    return sd * np.random.Generator(np.random.PCG64(seed)).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_forward(q, k, v, scale, ok):
+    """Per-element loops: q, k, v [N][d] python floats, ok[i][j] booleans."""
+    N, d = len(q), len(q[0])
+    O = [[0.0] * d for _ in range(N)]
+    L = [0.0] * N
+    for i in range(N):
+        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d))
+             for j in range(N) if ok[i][j]}
+        if not s:
+            L[i] = -math.inf
+            continue
+        m = max(s.values())
+        z = math.fsum(math.exp(x - m) for x in s.values())
+        L[i] = m + math.log(z)
+        for c in range(d):
+            O[i][c] = math.fsum(math.exp(s[j] - L[i]) * v[j][c] for j in s)
+    return np.array(O), np.array(L)
+
+
+def brute_mask(N, causal, bm, L):
+    return [[(not causal or j <= i) and (bm is None or bm[i // 128][j // 128] != 0)
+             and (L is None or j < L) for j in range(N)] for i in range(N)]
+
+
+@pytest.mark.parametrize("N,d,causal,kpad,bm", [
+    (1, 3, False, None, None),
+    (5, 3, False, None, None),
+    (7, 4, True, None, None),
+    (6, 2, False, 4, None),
+    (6, 2, True, 3, None),
+    (6, 2, False, 0, None),
+    (200, 2, False, None, [[1, 0], [1, 1]]),
+    (200, 2, True, 150, [[1, 1], [0, 1]]),
+])
+def test_forward_matches_brute_force(N, d, causal, kpad, bm):
+    q, k, v = rnd((N, d), 1), rnd((N, d), 2), rnd((N, d), 3)
+    scale = 0.7
+    bmask = None if bm is None else np.array(bm, dtype=np.uint8)
+    O, L = orc.head_forward(q, k, v, scale, causal, bmask, kpad)
+    Ob, Lb = brute_forward(q.tolist(), k.tolist(), v.tolist(),
+                           float(np.float32(scale)), brute_mask(N, causal, bm, kpad))
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(Lb)
+    assert np.array_equal(np.isfinite(L), fin)
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------- library routine (torch)
+
+def torch_reference(q, k, v, do, scale, ok):
+    import torch
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    bias = torch.zeros(ok.shape, dtype=torch.float64)
+    bias[~torch.tensor(ok)] = -math.inf
+    S = float(np.float32(scale)) * (tq @ tk.T) + bias
+    O = torch.softmax(S, dim=-1) @ tv
+    lse = torch.logsumexp(S, dim=-1)
+    (O * torch.tensor(do)).sum().backward()
+    return O.detach().numpy(), lse.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), \
+        tv.grad.numpy()
+
+
+@pytest.mark.parametrize("N,d,causal,kpad,bm", [
+    (64, 16, False, None, None),
+    (97, 32, True, None, None),
+    (150, 8, False, 77, None),
+    (256, 16, True, None, [[1, 0], [1, 1]]),
+    (256, 16, False, 200, [[1, 1], [0, 1]]),
+])
+def test_matches_torch_float64_autograd(N, d, causal, kpad, bm):
+    q, k, v, do = (rnd((N, d), s) for s in (11, 12, 13, 14))
+    scale = 1.0 / math.sqrt(d)
+    bmask = None if bm is None else np.array(bm, dtype=np.uint8)
+    ok = orc.allowed(np.arange(N), N, causal, bmask, kpad)
+    assert ok.any(axis=1).all()  # torch's softmax of an all -inf row is NaN
+    O, L, dq, dk, dv = torch_reference(q, k, v, do, scale, ok)
+    r = orc.head_backward(q, k, v, do, scale, causal, bmask, kpad)
+    for a, b in ((r["O"], O), (r["LSE"], L), (r["dQ"], dq), (r["dK"], dk), (r["dV"], dv)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-11)
+
+
+# --------------------------------------------------------------- closed forms
+
+def _golden_value(x):
+    if isinstance(x, str):
+        table = {"ln3": math.log(3), "ln4": math.log(4), "ln2": math.log(2),
+                 "0.75*ln3": 0.75 * math.log(3), "-2*ln3": -2 * math.log(3)}
+        return table[x]
+    return float(x)
+
+
+def _golden_array(rows):
+    return np.array([[_golden_value(x) for x in r] if isinstance(r, list) else _golden_value(r)
+                     for r in rows])
+
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_2x2.json")))
+    q, k, v, do = (_golden_array(g[n]) for n in ("q", "k", "v", "do"))
+    for case, exp in g["cases"].items():
+        r = orc.head_backward(q, k, v, do, g["scale"], causal=(case == "causal"))
+        for key, name in (("o", "O"), ("lse", "LSE"), ("dq", "dQ"), ("dk", "dK"), ("dv", "dV")):
+            np.testing.assert_allclose(r[name], _golden_array(exp[key]), rtol=0, atol=1e-14,
+                                       err_msg=f"{case}/{key}")
+
+
+def test_single_key_and_query():
+    q, k, v, do = (rnd((1, 8), s) for s in (1, 2, 3, 4))
+    r = orc.head_backward(q, k, v, do, 0.3)
+    np.testing.assert_allclose(r["O"], v, atol=1e-15)
+    np.testing.assert_allclose(r["LSE"], [float(np.float32(0.3)) * (q[0] @ k[0])], atol=1e-15)
+    np.testing.assert_allclose(r["dQ"], 0, atol=1e-15)
+    np.testing.assert_allclose(r["dK"], 0, atol=1e-15)
+    np.testing.assert_allclose(r["dV"], do, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_constant_rows(causal):
+    N, d = 300, 16
+    q, k = rnd((N, d), 5), rnd((N, d), 6)
+    row = rnd((d,), 7)
+    v = np.tile(row, (N, 1))
+    O, _ = orc.head_forward(q, k, v, 0.25, causal)
+    np.testing.assert_allclose(O, np.tile(row, (N, 1)), atol=1e-12)
+
+
+def test_causal_row_zero():
+    N, d = 130, 8
+    q, k, v = rnd((N, d), 8), rnd((N, d), 9), rnd((N, d), 10)
+    O, L = orc.head_forward(q, k, v, 0.5, causal=True)
+    np.testing.assert_allclose(O[0], v[0], atol=1e-15)
+    np.testing.assert_allclose(L[0], 0.5 * (q[0] @ k[0]), atol=1e-14)
+
+
+@pytest.mark.parametrize("kpad", [None, 100])
+def test_causal_zero_query_prefix_mean(kpad):
+    N, d = 260, 8
+    q = np.zeros((N, d))
+    k, v = rnd((N, d), 15), rnd((N, d), 16)
+    O, L = orc.head_forward(q, k, v, 0.125, causal=True, kv_len_b=kpad)
+    cnt = np.arange(1, N + 1) if kpad is None else np.minimum(np.arange(1, N + 1), kpad)
+    expect = np.cumsum(v, axis=0)[cnt - 1] / cnt[:, None]
+    np.testing.assert_allclose(O, expect, atol=1e-12)
+    np.testing.assert_allclose(L, np.log(cnt), atol=1e-13)
+
+
+# ----------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal,kpad,bm", [(False, None, None), (True, None, None),
+                                            (False, 90, None), (True, None, [[1, 0], [1, 1]])])
+def test_probability_rows_sum_to_one(causal, kpad, bm):
+    N = 160
+    d = N  # V = identity makes O equal to P
+    q, k = rnd((N, d), 20), rnd((N, d), 21)
+    bmask = None if bm is None else np.array(bm, dtype=np.uint8)
+    P, _ = orc.head_forward(q, k, np.eye(N), 0.1, causal, bmask, kpad)
+    ok = orc.allowed(np.arange(N), N, causal, bmask, kpad)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+    assert (P >= 0).all()
+    assert (P[~ok] == 0).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance_along_keys(causal):
+    N, d = 200, 12
+    q, k, v = rnd((N, d), 30), rnd((N, d), 31), rnd((N, d), 32)
+    u = rnd((d,), 33)
+    s = 0.2
+    O1, L1 = orc.head_forward(q, k, v, s, causal)
+    O2, L2 = orc.head_forward(q, k + u[None, :], v, s, causal)
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    np.testing.assert_allclose(L2 - L1, float(np.float32(s)) * (q @ u), atol=1e-12)
+
+
+def test_delta_two_ways():
+    N, d = 180, 16
+    q, k, v, do = (rnd((N, d), s) for s in (40, 41, 42, 43))
+    r = orc.head_backward(q, k, v, do, 0.25, causal=True)
+    P, _ = orc.head_forward(q, k, np.eye(N), 0.25, causal=True)  # V = I -> P
+    dP = do @ v.T
+    np.testing.assert_allclose(r["D"], (P * dP).sum(axis=1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["D"], orc.delta(r["O"], do), rtol=1e-12, atol=1e-12)
+
+
+def test_full_length_padding_is_no_padding():
+    N, d = 140, 8
+    q, k, v = rnd((N, d), 50), rnd((N, d), 51), rnd((N, d), 52)
+    a = orc.head_forward(q, k, v, 0.3, kv_len_b=N)
+    b = orc.head_forward(q, k, v, 0.3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_padding_equals_attention_on_prefix():
+    N, d, L = 150, 8, 61
+    q, k, v, do = (rnd((N, d), s) for s in (53, 54, 55, 56))
+    a = orc.head_backward(q, k, v, do, 0.3, kv_len_b=L)
+    # reference: N queries against the first L keys only
+    O, Lse = orc.head_forward(q, k[:L], v[:L], 0.3)
+    np.testing.assert_allclose(a["O"], O, atol=1e-12)
+    np.testing.assert_allclose(a["LSE"], Lse, atol=1e-12)
+    assert (a["dK"][L:] == 0).all() and (a["dV"][L:] == 0).all()
+
+
+def test_all_ones_block_mask_is_dense():
+    N, d = 300, 8
+    q, k, v = rnd((N, d), 60), rnd((N, d), 61), rnd((N, d), 62)
+    bm = np.ones((3, 3), dtype=np.uint8)
+    for causal in (False, True):
+        a = orc.head_forward(q, k, v, 0.4, causal, bm)
+        b = orc.head_forward(q, k, v, 0.4, causal)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_diagonal_block_mask_is_chunked_attention():
+    N, d = 300, 8
+    q, k, v, do = (rnd((N, d), s) for s in (63, 64, 65, 66))
+    bm = np.eye(3, dtype=np.uint8)
+    r = orc.head_backward(q, k, v, do, 0.4, blockmask=bm)
+    for c0 in range(0, N, 128):
+        sl = slice(c0, min(N, c0 + 128))
+        rc = orc.head_backward(q[sl], k[sl], v[sl], do[sl], 0.4)
+        for key in ("O", "LSE", "dQ", "dK", "dV"):
+            np.testing.assert_allclose(r[key][sl], rc[key], atol=1e-12)
+
+
+def test_fully_masked_rows():
+    N, d = 40, 8
+    q, k, v, do = (rnd((N, d), s) for s in (70, 71, 72, 73))
+    r = orc.head_backward(q, k, v, do, 0.5, kv_len_b=0)
+    assert (r["O"] == 0).all() and np.isneginf(r["LSE"]).all()
+    for key in ("dQ", "dK", "dV", "D"):
+        assert (r[key] == 0).all()
+    # a block table that leaves query block 1 with no key block
+    N = 200
+    q, k, v, do = (rnd((N, d), s) for s in (74, 75, 76, 77))
+    bm = np.array([[1, 0], [0, 0]], dtype=np.uint8)
+    r = orc.head_backward(q, k, v, do, 0.5, blockmask=bm)
+    assert (r["O"][128:] == 0).all() and np.isneginf(r["LSE"][128:]).all()
+    assert (r["dQ"][128:] == 0).all() and (r["dK"][128:] == 0).all()
+
+
+# ----------------------------------------------------------- finite differences
+
+def _loss(q, k, v, do, scale, causal, kpad):
+    O, _ = orc.head_forward(q, k, v, scale, causal, None, kpad)
+    return float((do * O).sum())
+
+
+@pytest.mark.parametrize("causal,kpad", [(False, None), (True, None), (False, 9)])
+def test_gradients_match_central_differences(causal, kpad):
+    N, d = 13, 5
+    q, k, v, do = (rnd((N, d), s) for s in (80, 81, 82, 83))
+    scale = 0.6
+    r = orc.head_backward(q, k, v, do, scale, causal, None, kpad)
+    rng = np.random.Generator(np.random.PCG64(84))
+    h = 1e-6
+    for name, x, g in (("q", q, r["dQ"]), ("k", k, r["dK"]), ("v", v, r["dV"])):
+        for _ in range(12):
+            i, c = int(rng.integers(N)), int(rng.integers(d))
+            xp, xm = x.copy(), x.copy()
+            xp[i, c] += h
+            xm[i, c] -= h
+            args = {"q": q, "k": k, "v": v}
+            fp = _loss(*(xp if n == name else args[n] for n in "qkv"), do, scale, causal, kpad)
+            fm = _loss(*(xm if n == name else args[n] for n in "qkv"), do, scale, causal, kpad)
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - g[i, c]) <= 1e-6 * max(1.0, abs(g[i, c])), (name, i, c, fd, g[i, c])
+
+
+# ------------------------------------------------------------- sampled entries
+
+def test_sampled_rows_agree_with_full():
+    B, H, N, d = 2, 2, 160, 16
+    q, k, v, do = (rnd((B, H, N, d), s) for s in (90, 91, 92, 93))
+    kv = np.array([160, 97], dtype=np.int32)
+    full = orc.backward(q, k, v, do, 0.25, causal=True, kv_len=kv)
+    sel = [(0, 1, 0), (1, 0, 5), (1, 1, 159), (0, 0, 128)]
+    O, L = orc.forward_rows(q, k, v, 0.25, sel, causal=True, kv_len=kv)
+    dq = orc.dq_rows(q, k, v, do, 0.25, sel, causal=True, kv_len=kv)
+    for n, (b, h, i) in enumerate(sel):
+        np.testing.assert_allclose(O[n], full["O"][b, h, i], atol=1e-13)
+        np.testing.assert_allclose(L[n], full["LSE"][b, h, i], atol=1e-13)
+        np.testing.assert_allclose(dq[n], full["dQ"][b, h, i], atol=1e-13)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
+    want = [1.0, -1.0, 0.0, -0.0, 3.3895313892515355e38, 9.183549615799121e-41, 3.140625]
+    np.testing.assert_array_equal(orc.widen_bf16(bits), want)
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _mutant_backward(kind):
+    """Copies of the oracle's backward with one plausible mistake each."""
+    def run(Qh, Kh, Vh, dOh, scale, causal=False):
+        N = Kh.shape[0]
+        s = float(np.float32(scale))
+        S = s * (Qh @ Kh.T)
+        S[~orc.allowed(np.arange(N), N, causal, None, None)] = -np.inf
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        P /= P.sum(axis=1, keepdims=True)
+        O = P @ Vh
+        D = (dOh * O).sum(axis=1)
+        dP = dOh @ Vh.T
+        dS = P * (dP - D[:, None])
+        dQ, dK, dV = s * (dS @ Kh), s * (dS.T @ Qh), P.T @ dOh
+        if kind == "drop_delta":
+            dS = P * dP
+            dQ, dK = s * (dS @ Kh), s * (dS.T @ Qh)
+        elif kind == "transposed_dk":
+            dK = s * (dS @ Qh)
+        elif kind == "missing_scale":
+            dQ = dS @ Kh
+        elif kind == "dv_not_transposed":
+            dV = P @ dOh
+        elif kind == "delta_sign":
+            dS = P * (dP + D[:, None])
+            dQ, dK = s * (dS @ Kh), s * (dS.T @ Qh)
+        return {"dQ": dQ, "dK": dK, "dV": dV}
+    return run
+
+
+@pytest.mark.parametrize("kind", ["drop_delta", "transposed_dk", "missing_scale",
+                                  "dv_not_transposed", "delta_sign"])
+def test_planted_backward_mistakes_are_caught(kind):
+    """Each mutant must disagree with the finite-difference gradient somewhere."""
+    N, d = 9, 9
+    q, k, v, do = (rnd((N, d), s) for s in (100, 101, 102, 103))
+    scale = 0.6
+    mut = _mutant_backward(kind)(q, k, v, do, scale, causal=True)
+    good = _mutant_backward("none")(q, k, v, do, scale, causal=True)
+    h = 1e-6
+    worst_mut, worst_good = 0.0, 0.0
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        g_key = {"q": "dQ", "k": "dK", "v": "dV"}[name]
+        for i in range(N):
+            for c in range(0, d, 4):
+                xp, xm = x.copy(), x.copy()
+                xp[i, c] += h
+                xm[i, c] -= h
+                args = {"q": q, "k": k, "v": v}
+                fp = _loss(*(xp if n == name else args[n] for n in "qkv"), do, scale, True, None)
+                fm = _loss(*(xm if n == name else args[n] for n in "qkv"), do, scale, True, None)
+                fd = (fp - fm) / (2 * h)
+                worst_mut = max(worst_mut, abs(fd - mut[g_key][i, c]))
+                worst_good = max(worst_good, abs(fd - good[g_key][i, c]))
+    assert worst_good < 1e-6
+    assert worst_mut > 1e-3
+
+
+def test_planted_forward_mistakes_are_caught():
+    """Forward mutants (no max subtraction is harmless; these are not) fail the pins."""
+    N, d = 260, 8
+    q = np.zeros((N, d))
+    k, v = rnd((N, d), 110), rnd((N, d), 111)
+    cnt = np.arange(1, N + 1)
+    expect = np.cumsum(v, axis=0) / cnt[:, None]
+    # causal off by one (j < i instead of j <= i) breaks the prefix-mean closed form
+    ok = np.tril(np.ones((N, N), dtype=bool), -1)
+    ok[0, 0] = True
+    S = np.where(ok, 0.0, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    assert np.abs(P @ v - expect).max() > 1e-3
+    # the real oracle passes it
+    O, _ = orc.head_forward(q, k, v, 0.125, causal=True)
+    assert np.abs(O - expect).max() < 1e-12
