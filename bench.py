@@ -1,0 +1,234 @@
+"""Bench: exact attention fwd and fwd+bwd on one MI355X, through libfa's C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole hot path once: fa_fwd_ex (O, LSE) then fa_bwd_ex (D, dQ, dK, dV),
+on seeded synthetic bf16 inputs already resident in HBM. Default workload: the long
+causal head set (B=1, H=16, N=16384, d=128), the configuration the headline metric is
+stated for. Prints one JSON line.
+
+FLOP convention (2 per multiply-add, allowed (query, key) pairs only):
+  fwd = 4 * pairs * d (Q K^T and P V); bwd = 10 * pairs * d (recomputed Q K^T, dO V^T,
+  P^T dO, dS K, dS^T Q); fwd+bwd = 14 * pairs * d.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "attention TFLOP/s fwd and fwd+bwd (bf16) at 1 GPU + % MFMA peak"
+
+
+def allowed_pairs(N, causal, blockmask, kv_len_b):
+    """Number of allowed (query, key) pairs of one head, from the mask definitions."""
+    rows = np.arange(N, dtype=np.int64)
+    lim = np.full(N, N, dtype=np.int64)
+    if causal:
+        lim = np.minimum(lim, rows + 1)
+    if kv_len_b is not None:
+        lim = np.minimum(lim, int(kv_len_b))
+    if blockmask is None:
+        return int(lim.sum())
+    nb = blockmask.shape[0]
+    total = 0
+    for kb in range(nb):
+        lo = kb * 128
+        cover = np.clip(lim - lo, 0, 128)              # keys of block kb below each row's limit
+        kept = blockmask[rows // 128, kb] != 0
+        total += int(cover[kept].sum())
+    return total
+
+
+def workload_pairs(x):
+    wl = x.wl
+    total = 0
+    for b in range(wl.B):
+        kv = None if x.kv_len is None else int(x.kv_len[b])
+        total += wl.H * allowed_pairs(wl.N, wl.causal, x.blockmask, kv)
+    return total
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal_16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-footprint", action="store_true")
+    return ap.parse_args()
+
+
+class Buffers:
+    def __init__(self, x, torch):
+        import exact_io_aware_46_amd as fa
+        wl = x.wl
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
+                torch.bfloat16)
+
+        self.wl = wl
+        self.q, self.k, self.v, self.do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
+        self.o = torch.empty_like(self.q)
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
+        self.delta = torch.empty_like(self.lse)
+        self.ws = torch.empty(fa.fa_bwd_workspace_bytes(wl.B, wl.H, wl.N, wl.d),
+                              dtype=torch.uint8, device="cuda")
+        self.bm = None if x.blockmask is None else torch.from_numpy(x.blockmask).cuda()
+        self.kv = None if x.kv_len is None else torch.from_numpy(x.kv_len).cuda()
+        self.fa = fa
+
+    def fwd(self):
+        w = self.wl
+        self.fa.fa_fwd_ex(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d,
+                          w.scale, w.causal, self.bm, self.kv)
+
+    def bwd(self):
+        w = self.wl
+        self.fa.fa_bwd_ex(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq, self.dk,
+                          self.dv, w.B, w.H, w.N, w.d, w.scale, w.causal, self.bm, self.kv,
+                          self.ws)
+
+    def pre(self):
+        w = self.wl
+        self.fa.fa_bwd_preprocess(self.o, self.do, self.delta, w.B, w.H, w.N, w.d)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def time_loop(torch, fn, steps, warmup):
+    """Mean milliseconds per call, HIP events on the stream the kernels run on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def footprint_sweep(torch, base):
+    """Peak device bytes of fwd+bwd buffers + workspace + calls at several N (same B, H, d)."""
+    from exact_io_aware_46_amd import inputs as inp
+    out = {}
+    for n in (2048, 4096, 8192, 16384):
+        wl = base.with_n(n)
+        x = inp.make_inputs(wl)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        before = torch.cuda.memory_allocated()
+        free0, _ = torch.cuda.mem_get_info()
+        buf = Buffers(x, torch)
+        buf.step()
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        out[str(n)] = {"peak_bytes": int(torch.cuda.max_memory_allocated() - before),
+                       "hip_free_delta_bytes": int(free0 - free1),
+                       "materialised_SP_bf16_bytes": 2 * wl.B * wl.H * n * n * 2}
+        del buf
+    ns = np.array([int(n) for n in out])
+    pk = np.array([out[str(n)]["peak_bytes"] for n in ns], dtype=np.float64)
+    slope, icpt = np.polyfit(ns, pk, 1)
+    resid = float(np.max(np.abs(pk - (slope * ns + icpt)) / pk))
+    return {"per_N": out, "linear_fit_bytes_per_token": float(slope),
+            "linear_fit_max_rel_residual": resid}
+
+
+def cpu_baseline(x, pairs_head):
+    """The fp64 oracle, timed on the host on one (b, h) head of the same workload."""
+    import threadpoolctl
+    from oracle import attention as orc
+    wl = x.wl
+    b, h = 0, 0
+    kv = None if x.kv_len is None else int(x.kv_len[b])
+    args = [orc.widen_bf16(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
+    t0 = time.perf_counter()
+    orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv)
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    return {"value": 14.0 * pairs_head * wl.d / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"one head (b={b}, h={h}) of {wl.name}: fp64 forward+backward with S and "
+                      f"P materialised (N={wl.N}, d={wl.d}), {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes, not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from exact_io_aware_46_amd import inputs as inp
+
+    wl = inp.WORKLOADS[args.workload]
+    x = inp.make_inputs(wl)
+    pairs = workload_pairs(x)
+    fl_fwd, fl_bwd = 4.0 * pairs * wl.d, 10.0 * pairs * wl.d
+    buf = Buffers(x, torch)
+
+    ms_step = time_loop(torch, buf.step, args.steps, args.warmup)
+    ms_fwd = time_loop(torch, buf.fwd, args.steps, args.warmup)
+    ms_bwd = time_loop(torch, buf.bwd, args.steps, args.warmup)
+    ms_pre = time_loop(torch, buf.pre, args.steps, args.warmup)
+    ms_bwd_main = max(ms_bwd - ms_pre, 1e-6)
+
+    tf_step = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
+    tf_fwd = fl_fwd / (ms_fwd * 1e-3) / 1e12
+    tf_bwd_main = fl_bwd / (ms_bwd_main * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "causal": wl.causal, "mask": wl.mask, "scale": wl.scale,
+                   "allowed_pairs": pairs},
+        "fwd_tflops": round(tf_fwd, 2), "fwd_ms": round(ms_fwd, 4),
+        "fwd_bwd_tflops": round(tf_step, 2),
+        "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_BF16_PEAK_TFLOPS, 2),
+        "fwd_bwd_pct_mfma_peak": round(100 * tf_step / MFMA_BF16_PEAK_TFLOPS, 2),
+        "bwd_ms": round(ms_bwd, 4), "bwd_preprocess_ms": round(ms_pre, 4),
+        "roofline": {"kernel": f"bwd_kernel<{wl.d}> + dq_convert (fa_bwd_ex minus "
+                               "fa_bwd_preprocess)",
+                     "bound": "mfma", "achieved": round(tf_bwd_main, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "roofline_fwd": {"kernel": f"fwd_kernel<{wl.d}>", "bound": "mfma",
+                         "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None},
+    }
+    if not args.no_footprint and wl.name == "long_causal_16k":
+        del buf
+        rec["footprint"] = footprint_sweep(torch, wl)
+    if not args.no_cpu_baseline:
+        kv0 = None if x.kv_len is None else int(x.kv_len[0])
+        rec["cpu_baseline"] = cpu_baseline(x, allowed_pairs(wl.N, wl.causal, x.blockmask, kv0))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,162 @@
-"""libfa: exact, tiled, fused attention for MI355X (gfx950)."""
+"""libfa: exact, tiled, fused attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/fa.h``. Functions with the C names take
+torch tensors (device memory owned by the caller) and marshal them to pointers; every
+step of the computation runs in the HIP kernels of ``libfa.so``. There is no fallback:
+if the library is not built, or a tensor is not on the GPU, the call raises.
+
+    python -m exact_io_aware_46_amd.build   # builds exact_io_aware_46_amd/libfa.so
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED_D",
+                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_LAUNCH", 7: "FA_ERR_ALIAS"}
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
+    "fa_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
+    "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P,
+                       _P]),
+    "fa_strerror": (ctypes.c_char_p, [_I]),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({strerror(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m exact_io_aware_46_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+# ------------------------------------------------------------- marshalling
+
+def _dev_ptr(t, name):
+    """Device pointer of a torch tensor (None -> NULL). Raises for host tensors."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, stream=None):
+    _check(lib().fa_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                        _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
+                        int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                        _stream_ptr(stream)), "fa_fwd")
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
+              stream=None):
+    _check(lib().fa_fwd_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                           _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
+                           int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                           _dev_ptr(kv_len, "kv_len"), _stream_ptr(stream)), "fa_fwd_ex")
+
+
+def fa_bwd_preprocess(o, dO, delta, B, H, N, d, stream=None):
+    _check(lib().fa_bwd_preprocess(_dev_ptr(o, "o"), _dev_ptr(dO, "dO"),
+                                   _dev_ptr(delta, "delta"), B, H, N, d,
+                                   _stream_ptr(stream)), "fa_bwd_preprocess")
+
+
+def fa_bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
+           workspace=None, stream=None):
+    _check(lib().fa_bwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                        _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
+                        _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N, d,
+                        float(scale), int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                        _dev_ptr(workspace, "workspace"), _stream_ptr(stream)), "fa_bwd")
+
+
+def fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
+              kv_len=None, workspace=None, stream=None):
+    _check(lib().fa_bwd_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                           _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
+                           _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N,
+                           d, float(scale), int(bool(causal)),
+                           _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
+                           _dev_ptr(workspace, "workspace"), _stream_ptr(stream)), "fa_bwd_ex")
+
+
+# ------------------------------------------------- allocating convenience layer
+
+def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, stream=None):
+    """q, k, v: bf16 GPU tensors [B, H, N, d]. Returns (o, lse) newly allocated."""
+    import torch
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=None,
+             workspace=None, stream=None):
+    """Returns (dq, dk, dv) newly allocated; allocates the workspace if none is given."""
+    import torch
+    B, H, N, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len,
+              workspace, stream)
+    return dq, dk, dv

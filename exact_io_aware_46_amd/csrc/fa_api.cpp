@@ -1,0 +1,167 @@
+// C-ABI front end of libfa: argument validation, workspace layout, kernel dispatch.
+// All checks run on the host before any HIP call; nothing is allocated here.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape limits: every flat row index (B*H*N) and every per-head element offset (N*d) must
+// fit in a signed 32-bit int, and the grid size in a 32-bit unsigned.
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  const long long rows = (long long)B * H * N;
+  if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || scale == 0.f) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+inline Range span(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the problem must fit 32-bit indexing)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse/delta 4, workspace 256)";
+    case FA_ERR_SCALE: return "scale must be finite and nonzero";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || (kv_len && !aligned(kv_len, 4)))
+    return FA_ERR_ALIGN;
+  const size_t tbytes = (size_t)B * H * N * d * 2, lbytes = (size_t)B * H * N * 4;
+  const Range ro = span(o, tbytes), rl = span(lse, lbytes);
+  if (overlap(ro, rl)) return FA_ERR_ALIAS;
+  for (const void* in : {(const void*)q, (const void*)k, (const void*)v})
+    if (overlap(ro, span(in, tbytes)) || overlap(rl, span(in, tbytes))) return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.blockmask = blockmask;
+  p.kv_len = kv_len;
+  p.B = B; p.H = H; p.N = N;
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  if (fa::launch_fwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+int fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+           void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
+}
+
+int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
+                      int d, void* stream) {
+  if (!o || !dO || !delta) return FA_ERR_NULL;
+  const int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(delta, 4)) return FA_ERR_ALIGN;
+  const size_t tbytes = (size_t)B * H * N * d * 2;
+  const Range rd = span(delta, (size_t)B * H * N * 4);
+  if (overlap(rd, span(o, tbytes)) || overlap(rd, span(dO, tbytes))) return FA_ERR_ALIAS;
+  if (fa::launch_bwd_preprocess(o, dO, delta, nullptr, B * H * N, d,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * 4, kWsAlign) + rows * (size_t)d * 4;
+}
+
+int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+              const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* workspace, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dO, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, kWsAlign) || (kv_len && !aligned(kv_len, 4)))
+    return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * N;
+  const size_t tbytes = rows * d * 2;
+  const Range outs[4] = {span(dq, tbytes), span(dk, tbytes), span(dv, tbytes),
+                         span(workspace, fa_bwd_workspace_bytes(B, H, N, d))};
+  const Range ins[6] = {span(q, tbytes), span(k, tbytes), span(v, tbytes),
+                        span(o, tbytes), span(dO, tbytes), span(lse, rows * 4)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return FA_ERR_ALIAS;
+    for (int b = 0; b < 6; ++b)
+      if (overlap(outs[a], ins[b])) return FA_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  fa::BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.dO = dO;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.blockmask = blockmask;
+  p.kv_len = kv_len;
+  p.delta = reinterpret_cast<float*>(ws);
+  p.dq_accum = reinterpret_cast<float*>(ws + round_up(rows * 4, kWsAlign));
+  p.B = B; p.H = H; p.N = N;
+  p.scale = scale;
+  p.causal = causal ? 1 : 0;
+  if (fa::launch_bwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+           const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv, int B,
+           int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+           void* workspace, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                   nullptr, workspace, stream);
+}
+
+}  // extern "C"

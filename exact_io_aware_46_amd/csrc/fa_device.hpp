@@ -1,0 +1,103 @@
+// Device-side helpers shared by the libfa kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kInf = __builtin_huge_valf();
+
+// 32x32 output tile, 16-deep contraction, bf16 inputs, fp32 accumulate.
+// Operand layout (A: M x K, B: K x N): lane l holds row/column (l % 32) and a group of
+// 8 contraction indices selected by (l / 32). Output: lane l holds column (l % 32) and
+// rows 8*(i/4) + 4*(l/32) + (i%4) for accumulator element i = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row permutation applied to the M operand of a score MFMA: swapping bits 2 and 3 of the
+// row index makes accumulator elements 8*g .. 8*g+7 of lane half h hold the 8 consecutive
+// rows 16*g + 8*h .. 16*g + 8*h + 7, which is exactly the contraction group a lane of the
+// following MFMA must supply. It is an involution.
+__device__ __forceinline__ int perm_row(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Row of the 32-row block held by accumulator element i in lane half h (after perm_row).
+__device__ __forceinline__ int acc_row(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return bf16_bits(a) | (bf16_bits(b) << 16);
+}
+
+// Eight fp32 accumulator elements [base, base+8) -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int base) {
+  u32x4 r;
+  r[0] = pack_bf16(x[base + 0], x[base + 1]);
+  r[1] = pack_bf16(x[base + 2], x[base + 3]);
+  r[2] = pack_bf16(x[base + 4], x[base + 5]);
+  r[3] = pack_bf16(x[base + 6], x[base + 7]);
+  return as_bf16x8(r);
+}
+
+// Combine a per-lane value with the lane 32 positions away (lanes l and l^32).
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four rows (same 8 columns) -> eight 64-bit words, word e holding column e of rows 0..3.
+// Used to write a row-major tile into a transposed LDS layout with 8-byte stores.
+__device__ __forceinline__ u32x2 transpose_col(const u32x4 (&rows)[4], int e) {
+  const int w = e >> 1;
+  u32x2 out;
+  if ((e & 1) == 0) {
+    out[0] = (rows[0][w] & 0xffffu) | (rows[1][w] << 16);
+    out[1] = (rows[2][w] & 0xffffu) | (rows[3][w] << 16);
+  } else {
+    out[0] = (rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u);
+    out[1] = (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u);
+  }
+  return out;
+}
+
+// Transposed tiles are stored as rows of 16-byte chunks; chunk c of row r sits at
+// position c ^ ((r >> 4) & 7). Rows read together by one MFMA operand load (16
+// consecutive rows) share the same XOR, and the 8-byte transposing stores spread over
+// all banks.
+__device__ __forceinline__ int tchunk(int row, int chunk) { return chunk ^ ((row >> 4) & 7); }
+
+}  // namespace fa

@@ -1,0 +1,47 @@
+// Launch parameters shared between the C-ABI front end and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const uint8_t* blockmask;  // [nb][nb] or null
+  const int32_t* kv_len;     // [B] or null
+  int B, H, N;
+  float scale;
+  int causal;
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dO;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const uint8_t* blockmask;
+  const int32_t* kv_len;
+  float* delta;     // [B][H][N]
+  float* dq_accum;  // [B][H][N][d]
+  int B, H, N;
+  float scale;
+  int causal;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* delta,
+                                 float* dq_accum, int rows, int d, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
+
+}  // namespace fa

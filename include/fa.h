@@ -1,0 +1,109 @@
+/*
+ * libfa -- exact, tiled, fused scaled-dot-product attention for AMD MI355X (gfx950).
+ *
+ * What is computed (per batch entry b and head h, N queries, N keys, head dim d):
+ *   S = scale * Q K^T, masked to -inf where a key is not allowed for a query;
+ *   P = softmax(S) along keys;  O = P V;  LSE_i = ln sum_j exp(S_ij).
+ * This is standard attention as described on the page "FlashAttention学习笔记"
+ * (amentiraz.github.io), section Forward运作流程 / 标准attention计算 and 标准Safe softmax;
+ * the method returns exactly that output while never writing S or P to HBM
+ * ("高效注意力算法实现 (FlashAttention)", apxml.com, section FlashAttention：融合算子与分块
+ * 处理, and 优势与影响). The backward pass recomputes P from the saved per-row statistic
+ * instead of storing it (report on "FlashAttention：一种基于I/O感知的快速且内存高效的自注意力
+ * 算法", fmread.com, section 算法设计); here that statistic is LSE in natural log.
+ *
+ * Masks (any combination; a key is allowed iff every active mask allows it):
+ *   causal     key j allowed for query i iff j <= i;
+ *   blockmask  uint8 table [nb][nb], nb = ceil(N/128): entry [i/128][j/128] != 0 keeps the
+ *              128x128 block (block-sparse attention: the report's 研究亮点 item 3 and the
+ *              abstract of "FlashAttention: Fast and Memory-Efficient Exact Attention with
+ *              IO-Awareness"), the same table for every (b, h);
+ *   kv_len     int32 [B]: keys j >= kv_len[b] are masked (key padding). Values must lie in
+ *              [0, N]; they are read on the device and not validated on the host.
+ * A query row with no allowed key gets O = 0, LSE = -inf, and contributes no gradient.
+ *
+ * Data layout and ownership:
+ *   q, k, v, o, dO, dq, dk, dv: contiguous [B][H][N][d] bfloat16 (raw bits, uint16),
+ *     DEVICE pointers, 16-byte aligned.
+ *   lse, delta: contiguous [B][H][N] float32, DEVICE pointers, 4-byte aligned.
+ *   blockmask, kv_len: DEVICE pointers or NULL (NULL = mask not used).
+ *   workspace: DEVICE pointer, 256-byte aligned, at least fa_bwd_workspace_bytes() bytes.
+ *   The caller allocates and frees everything; the library allocates nothing and keeps no
+ *   global mutable state. Outputs must not alias inputs or each other.
+ *   stream: a hipStream_t (NULL = the default stream). All work is enqueued asynchronously
+ *   on it; inputs must stay valid and unmodified until the stream has run the work.
+ *   Supported head dims: d in {64, 128}. scale must be finite and nonzero (negative values
+ *   are allowed).
+ *
+ * Errors: every entry point validates its arguments on the host before any HIP call and
+ * returns a nonzero fa_status without launching anything when they are invalid. A failed
+ * kernel launch returns FA_ERR_LAUNCH. Faults during execution surface at the caller's
+ * next synchronisation of the stream.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t fa_bf16; /* raw bfloat16 bits */
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,           /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,          /* B, H or N < 1, or the problem is too large          */
+  FA_ERR_UNSUPPORTED_D = 3,  /* d is not 64 or 128                                  */
+  FA_ERR_ALIGN = 4,          /* a pointer does not have the alignment stated above  */
+  FA_ERR_SCALE = 5,          /* scale is zero, NaN or infinite                      */
+  FA_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch            */
+  FA_ERR_ALIAS = 7           /* an output buffer overlaps an input or another output */
+};
+
+/* Forward. Writes O [B][H][N][d] (bf16) and LSE [B][H][N] (fp32, natural log).
+ * causal: 0 or 1. blockmask: NULL or device uint8 [ceil(N/128)][ceil(N/128)]. */
+int fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+           void* stream);
+
+/* Forward with key padding: as fa_fwd, plus kv_len (NULL or device int32 [B]). */
+int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* stream);
+
+/* Backward preprocess: delta[b][h][i] = sum_c dO[b][h][i][c] * O[b][h][i][c], summed in
+ * fp32 over the given bf16 O and dO. This is the row statistic D of the softmax gradient
+ * dS = P * (dP - D). fa_bwd runs it itself; it is exported for callers that want D. */
+int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
+                      int d, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: delta (fp32 [B][H][N]) and a fp32 dQ accumulator
+ * ([B][H][N][d]). Linear in N. Returns 0 for invalid shapes. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward. Inputs: q, k, v, the forward's o and lse, and dO = dL/dO. Outputs dq, dk, dv
+ * (bf16). Recomputes P from lse; no N x N matrix is stored. The workspace contents on
+ * entry are ignored. dq is accumulated with fp32 atomics, so its low bits may differ from
+ * run to run; o, lse, dk and dv do not depend on scheduling. */
+int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+           const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv, int B,
+           int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+           void* workspace, void* stream);
+
+/* Backward with key padding (kv_len: NULL or device int32 [B]). */
+int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+              const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports exactly what include/fa.h
+declares, and rejects invalid arguments on the host before any HIP call (so every call
+here returns an error code; no call here has valid arguments, none reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_46_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, never-dereferenced device addresses (validation only looks at their values).
+A = 0x7F0000000000
+T_BYTES = 1 << 30  # spacing that keeps fake buffers disjoint
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def exported_functions():
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.lib()
+
+
+def test_library_exports_exactly_the_header(lib):
+    decl = declared_functions()
+    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_preprocess", "fa_bwd_workspace_bytes",
+                    "fa_fwd", "fa_fwd_ex", "fa_strerror"]
+    assert exported_functions() == decl
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_strerror(lib):
+    for st in range(8):
+        assert len(fa.strerror(st)) > 0
+    assert fa.strerror(99) == "unknown status"
+
+
+def ptrs(n):
+    return [A + i * T_BYTES for i in range(n)]
+
+
+def fwd(lib, *, q=None, k=None, v=None, o=None, lse=None, B=1, H=1, N=64, d=64, scale=0.125,
+        causal=0, kv=None):
+    p = ptrs(5)
+    args = [p[0] if q is None else q, p[1] if k is None else k, p[2] if v is None else v,
+            p[3] if o is None else o, p[4] if lse is None else lse]
+    return lib.fa_fwd_ex(*args, B, H, N, d, scale, causal, None, kv, None)
+
+
+def test_fwd_null_pointers(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: 0}) == 1
+
+
+@pytest.mark.parametrize("B,H,N", [(0, 1, 64), (1, 0, 64), (1, 1, 0), (-1, 1, 64),
+                                   (1 << 16, 1 << 10, 1 << 10)])
+def test_fwd_bad_shape(lib, B, H, N):
+    assert fwd(lib, B=B, H=H, N=N) == 2
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 256, -64])
+def test_fwd_unsupported_head_dim(lib, d):
+    assert fwd(lib, d=d) == 3
+
+
+def test_fwd_misaligned(lib):
+    assert fwd(lib, q=A + 8) == 4
+    assert fwd(lib, o=A + 3 * T_BYTES + 2) == 4
+    assert fwd(lib, lse=A + 4 * T_BYTES + 2) == 4
+    assert fwd(lib, kv=A + 6 * T_BYTES + 1) == 4
+
+
+@pytest.mark.parametrize("scale", [0.0, float("nan"), float("inf"), -float("inf")])
+def test_fwd_bad_scale(lib, scale):
+    assert fwd(lib, scale=scale) == 5
+
+
+def test_fwd_alias(lib):
+    assert fwd(lib, o=A) == 7                     # o overlaps q
+    assert fwd(lib, lse=A + 3 * T_BYTES + 64) == 7  # lse inside o
+
+
+def bwd(lib, over=None, B=1, H=1, N=64, d=64, scale=0.125, ws_off=0):
+    p = ptrs(10)
+    p[9] += ws_off
+    if over:
+        for i, val in over.items():
+            p[i] = val
+    return lib.fa_bwd_ex(*p[:9], B, H, N, d, scale, 0, None, None, p[9], None)
+
+
+def test_bwd_errors(lib):
+    for i in range(10):
+        assert bwd(lib, {i: 0}) == 1
+    assert bwd(lib, B=0) == 2
+    assert bwd(lib, d=80) == 3
+    assert bwd(lib, {0: A + 8}) == 4
+    assert bwd(lib, ws_off=16) == 4                  # workspace needs 256-byte alignment
+    assert bwd(lib, scale=float("nan")) == 5
+    assert bwd(lib, {6: A + 3 * T_BYTES}) == 7       # dq aliases o
+    assert bwd(lib, {7: A + 6 * T_BYTES}) == 7       # dk aliases dq
+    assert bwd(lib, {9: A + 2 * T_BYTES}) == 7       # workspace aliases v
+
+
+def test_preprocess_errors(lib):
+    assert lib.fa_bwd_preprocess(None, A, A + T_BYTES, 1, 1, 8, 64, None) == 1
+    assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 2 * T_BYTES, 1, 1, 8, 48, None) == 3
+    assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 2, 1, 1, 8, 64, None) == 4
+    assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 4, 1, 1, 8, 64, None) == 7
+
+
+def test_workspace_bytes_linear_in_n(lib):
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 100) == 0
+    w = [fa.fa_bwd_workspace_bytes(1, 16, n, 128) for n in (2048, 4096, 8192, 16384)]
+    assert w[0] == 16 * 2048 * 4 + 16 * 2048 * 128 * 4
+    assert [x / w[0] for x in w] == [1, 2, 4, 8]
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x, x, torch.zeros((1, 1, 8)), 1, 1, 8, 64, 0.125, stream=0)

@@ -1,0 +1,250 @@
+"""GPU parity: libfa (HIP, gfx950) against the fp64 oracle on identical seeded inputs.
+
+Small shapes are compared element by element over every output; they span several
+tiles and ragged tails (N not a multiple of 64/128), every mask mode and their
+intersections, fully masked rows, both head dims and a negative scale. The five full
+workloads are run in the same launch configuration as the bench; the largest two are
+compared on sampled rows (O, LSE, dQ computed row by row by the oracle) and on one
+whole head (dK, dV).
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_46_amd import inputs as inp
+from oracle import attention as orc
+from tests.gpu_util import Run, check_all, check_grad, check_lse, check_o, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_all(q, k, v, do, scale, causal=False, bm=None, kv=None):
+    return orc.backward(q, k, v, do, scale, causal, bm, kv)
+
+
+def run_and_check(q, k, v, do, scale, causal=False, bm=None, kv=None, what=""):
+    say(f"[parity] {what} shape={q.shape} causal={causal} bm={bm is not None} kv={kv}")
+    res = Run(q, k, v, do, scale, causal, bm, kv).result()
+    ref = oracle_all(q, k, v, do, scale, causal, bm, kv)
+    check_all(res, ref, what)
+    return res, ref
+
+
+# ------------------------------------------------------------- small shapes
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 64, 127, 129, 255, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_dense_and_causal(d, N, causal):
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=1000 + N + d)
+    run_and_check(q, k, v, do, float(np.float32(1 / np.sqrt(d))), causal,
+                  what=f"small d={d} N={N}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_padding_with_edges(d, causal):
+    N = 300
+    q, k, v, do = inp.custom_inputs(4, 2, N, d, seed=77)
+    kv = np.array([300, 1, 129, 0], dtype=np.int32)  # full, one key, ragged, empty
+    res, ref = run_and_check(q, k, v, do, 0.125, causal, kv=kv, what=f"kpad d={d}")
+    # batch 3 has no key at all: O = 0, LSE = -inf, gradients exactly zero
+    assert (res["O"][3] == 0).all() and np.isneginf(res["LSE"][3]).all()
+    for g in ("dQ", "dK", "dV"):
+        assert (res[g][3] == 0).all()
+    # keys past the valid length get exactly zero dK, dV
+    for b, L in enumerate(kv):
+        assert (res["dK"][b, :, L:] == 0).all() and (res["dV"][b, :, L:] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_with_empty_row_and_column(d, causal):
+    N = 300  # 3 blocks, the last one ragged
+    q, k, v, do = inp.custom_inputs(2, 3, N, d, seed=91)
+    bm = np.array([[1, 0, 1],
+                   [0, 0, 0],    # query block 1 sees nothing: fully masked rows
+                   [1, 0, 1]], dtype=np.uint8)  # key block 1 is never used
+    res, ref = run_and_check(q, k, v, do, 0.1, causal, bm=bm, what=f"block d={d}")
+    assert np.isneginf(res["LSE"][:, :, 128:256]).all()
+    assert (res["dK"][:, :, 128:256] == 0).all() and (res["dV"][:, :, 128:256] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_all_masks_together(d):
+    N = 520
+    q, k, v, do = inp.custom_inputs(3, 2, N, d, seed=5)
+    rng = np.random.Generator(np.random.PCG64(6))
+    bm = inp.draw_block_mask(rng, N, 0.5)
+    kv = np.array([520, 333, 200], dtype=np.int32)
+    run_and_check(q, k, v, do, 0.09, True, bm=bm, kv=kv, what=f"all masks d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_negative_scale_and_wide_scores(d):
+    N = 200
+    q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=17, dist="wide")
+    run_and_check(q, k, v, do, -0.2, False, what=f"negative scale d={d}")
+    run_and_check(q, k, v, do, 0.2, True, what=f"wide causal d={d}")
+
+
+# ------------------------------------------------------- closed forms on GPU
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_zero_query_lse_indexing(d):
+    """Q = 0 under a causal mask: LSE_i = ln(i+1) and O_i = mean(V_0..V_i); pins the row
+    index of every LSE the kernel writes."""
+    N = 1000
+    _, k, v, do = inp.custom_inputs(1, 2, N, d, seed=23)
+    q = np.zeros_like(k)
+    say(f"[parity] causal Q=0 d={d}")
+    res = Run(q, k, v, do, 0.125, True).result()
+    cnt = np.arange(1, N + 1)
+    np.testing.assert_allclose(res["LSE"], np.broadcast_to(np.log(cnt), res["LSE"].shape),
+                               atol=1e-5, rtol=0)
+    vf = orc.widen_bf16(v)
+    expect = np.cumsum(vf, axis=2) / cnt[None, None, :, None]
+    check_o(res["O"], expect, "prefix mean")
+
+
+# ----------------------------------------------------------- bit-exactness
+
+def _bits_equal(a, b):
+    return a.view(torch.int16).equal(b.view(torch.int16)) if a.dtype == torch.bfloat16 \
+        else torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_all_ones_block_mask_is_bitwise_dense(d):
+    N = 384
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=31)
+    say(f"[bitexact] ones mask d={d}")
+    a = Run(q, k, v, do, 0.125, True)
+    b = Run(q, k, v, do, 0.125, True, blockmask=np.ones((3, 3), np.uint8))
+    for name in ("o", "lse", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+    check_grad(to_f64(b.dq_), to_f64(a.dq_), "dQ")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_padding_poison_is_bitwise_invisible(d):
+    """Keys past kv_len filled with NaN change nothing (O, LSE, dK, dV bitwise)."""
+    N = 300
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=37)
+    kv = np.array([211, 64], dtype=np.int32)
+    kp, vp = k.copy(), v.copy()
+    for b, L in enumerate(kv):
+        kp[b, :, L:] = 0x7FC0  # NaN
+        vp[b, :, L:] = 0xFFC0
+    say(f"[bitexact] padding poison d={d}")
+    a = Run(q, k, v, do, 0.125, False, kv_len=kv)
+    b = Run(q, kp, vp, do, 0.125, False, kv_len=kv)
+    for name in ("o", "lse", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+    assert torch.isfinite(b.dq_.float()).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_skipped_block_poison_is_bitwise_invisible(d):
+    """K/V of a key block that query block 0 masks out are poisoned with NaN: rows of
+    query block 0 are bitwise unchanged."""
+    N = 384
+    q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=41)
+    bm = np.ones((3, 3), np.uint8)
+    bm[0, 2] = 0
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, 256:] = 0x7FC0
+    vp[:, :, 256:] = 0x7FC0
+    say(f"[bitexact] block poison d={d}")
+    a = Run(q, k, v, None, 0.125, False, blockmask=bm, backward=False)
+    b = Run(q, kp, vp, None, 0.125, False, blockmask=bm, backward=False)
+    assert _bits_equal(a.o[:, :, :128].contiguous(), b.o[:, :, :128].contiguous())
+    assert _bits_equal(a.lse[:, :, :128].contiguous(), b.lse[:, :, :128].contiguous())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_future_poison_is_bitwise_invisible(d):
+    """Large finite values in keys/values after position t leave rows < t bitwise equal."""
+    N, t = 400, 203
+    q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=43)
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, t:] = inp.f32_to_bf16_bits(np.full(kp[:, :, t:].shape, 3e4, np.float32))
+    vp[:, :, t:] = inp.f32_to_bf16_bits(np.full(vp[:, :, t:].shape, -3e4, np.float32))
+    say(f"[bitexact] causal poison d={d}")
+    a = Run(q, k, v, None, 0.125, True, backward=False)
+    b = Run(q, kp, vp, None, 0.125, True, backward=False)
+    assert _bits_equal(a.o[:, :, :t].contiguous(), b.o[:, :, :t].contiguous())
+    assert _bits_equal(a.lse[:, :, :t].contiguous(), b.lse[:, :, :t].contiguous())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_and_dkdv_are_deterministic(d):
+    N = 640
+    q, k, v, do = inp.custom_inputs(2, 3, N, d, seed=47)
+    say(f"[bitexact] determinism d={d}")
+    a = Run(q, k, v, do, 0.125, True)
+    b = Run(q, k, v, do, 0.125, True)
+    for name in ("o", "lse", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_preprocess_delta(d):
+    import exact_io_aware_46_amd as fa
+    N = 333
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=53)
+    say(f"[parity] preprocess d={d}")
+    r = Run(q, k, v, do, 0.125, False, backward=False)
+    dO = r.do
+    delta = torch.empty((2, 2, N), dtype=torch.float32, device="cuda")
+    fa.fa_bwd_preprocess(r.o, dO, delta, 2, 2, N, d)
+    torch.cuda.synchronize()
+    o_bits = r.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = orc.delta(o_bits, do)
+    np.testing.assert_allclose(delta.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
+# --------------------------------------------------------- the five workloads
+
+def _sample_rows(wl, n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sel = {(0, 0, 0), (wl.B - 1, wl.H - 1, wl.N - 1), (0, wl.H - 1, 127), (wl.B - 1, 0, 128)}
+    while len(sel) < n:
+        sel.add((int(rng.integers(wl.B)), int(rng.integers(wl.H)), int(rng.integers(wl.N))))
+    return sorted(sel)
+
+
+@pytest.mark.parametrize("name", ["single_head_256", "gpt2s_causal_1k", "bertl_kpad_512"])
+def test_workload_full_compare(name):
+    wl = inp.WORKLOADS[name]
+    x = inp.make_inputs(wl)
+    run_and_check(x.q, x.k, x.v, x.do, wl.scale, wl.causal, x.blockmask, x.kv_len,
+                  what=name)
+
+
+@pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k"])
+def test_workload_sampled_compare(name):
+    wl = inp.WORKLOADS[name]
+    x = inp.make_inputs(wl)
+    say(f"[parity] {name} (sampled rows + one full head)")
+    res = Run(x.q, x.k, x.v, x.do, wl.scale, wl.causal, x.blockmask, x.kv_len).result()
+    for key in res:
+        assert np.isfinite(res[key]).all(), key
+    sel = _sample_rows(wl, 48, wl.seed)
+    o_ref, l_ref = orc.forward_rows(x.q, x.k, x.v, wl.scale, sel, wl.causal, x.blockmask,
+                                    x.kv_len)
+    dq_ref = orc.dq_rows(x.q, x.k, x.v, x.do, wl.scale, sel, wl.causal, x.blockmask, x.kv_len)
+    idx = tuple(np.array(sel).T)
+    check_o(res["O"][idx], o_ref, name)
+    check_lse(res["LSE"][idx], l_ref, name)
+    check_grad(res["dQ"][idx], dq_ref, "dQ", name)
+    b, h = wl.B - 1, wl.H // 2
+    say(f"[parity] {name} full head ({b},{h}) oracle")
+    kv_b = None if x.kv_len is None else int(x.kv_len[b])
+    ref = orc.head_backward(orc.widen_bf16(x.q[b, h]), orc.widen_bf16(x.k[b, h]),
+                            orc.widen_bf16(x.v[b, h]), orc.widen_bf16(x.do[b, h]), wl.scale,
+                            wl.causal, x.blockmask, kv_b)
+    check_o(res["O"][b, h], ref["O"], name)
+    check_lse(res["LSE"][b, h], ref["LSE"], name)
+    for g in ("dQ", "dK", "dV"):
+        check_grad(res[g][b, h], ref[g], g, name)
