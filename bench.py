@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--workload", default="long_causal_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-footprint", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (a kernel of known "
+                         "traffic, used to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -155,22 +158,61 @@ def footprint_sweep(torch, base):
             "linear_fit_max_rel_residual": resid}
 
 
-def cpu_baseline(x, pairs_head):
-    """The fp64 oracle, timed on the host on one (b, h) head of the same workload."""
+KERNEL_SOURCES = {"fwd_kernel": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.h"],
+                  "bwd_kernel": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.h"]}
+
+
+def source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "exact_io_aware_46_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kind, kernels):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (profiles/traffic_<workload>.md, copy-calibrated), or None when there is no summary
+    or the kernel's sources have changed since the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- traffic-json: (.*) -->", open(path).read())
+    if not m:
+        return None
+    blob = json.loads(m.group(1))
+    if blob.get("source_sha256", {}).get(kind) != source_hash(kind):
+        return None
+    try:
+        return int(sum(blob["kernels"][k]["read_bytes"] + blob["kernels"][k]["write_bytes"]
+                       for k in kernels))
+    except KeyError:
+        return None
+
+
+def cpu_baseline(x, heads=4):
+    """The fp64 oracle (as it stands), timed on the host on the first ``heads`` (b, h)
+    heads of the same workload; rate = their allowed-pair FLOP / wall time."""
     import threadpoolctl
     from oracle import attention as orc
     wl = x.wl
-    b, h = 0, 0
-    kv = None if x.kv_len is None else int(x.kv_len[b])
-    args = [orc.widen_bf16(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
+    sel = [(b, h) for b in range(wl.B) for h in range(wl.H)][:heads]
+    flop = 0.0
     t0 = time.perf_counter()
-    orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv)
+    for b, h in sel:
+        kv = None if x.kv_len is None else int(x.kv_len[b])
+        args = [orc.widen_bf16(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
+        orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv)
+        flop += 14.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv) * wl.d
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    return {"value": 14.0 * pairs_head * wl.d / dt / 1e12, "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"one head (b={b}, h={h}) of {wl.name}: fp64 forward+backward with S and "
-                      f"P materialised (N={wl.N}, d={wl.d}), {dt:.1f} s wall"}
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(sel)} of {wl.B * wl.H} heads of {wl.name} (N={wl.N}, d={wl.d}): "
+                      f"fp64 forward+backward with S and P materialised, numpy/OpenBLAS, "
+                      f"{dt:.1f} s wall"}
 
 
 def main():
@@ -183,6 +225,12 @@ def main():
     import torch
     from exact_io_aware_46_amd import inputs as inp
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = inp.WORKLOADS[args.workload]
     x = inp.make_inputs(wl)
     pairs = workload_pairs(x)
@@ -215,18 +263,20 @@ def main():
                                "fa_bwd_preprocess)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, "bwd_kernel",
+                                                 [f"bwd_kernel<{wl.d}>", "dq_convert_kernel"])},
         "roofline_fwd": {"kernel": f"fwd_kernel<{wl.d}>", "bound": "mfma",
                          "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic(wl.name, "fwd_kernel",
+                                                     [f"fwd_kernel<{wl.d}, {64 if wl.d == 128 else 128}>"])},
     }
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf
         rec["footprint"] = footprint_sweep(torch, wl)
     if not args.no_cpu_baseline:
-        kv0 = None if x.kv_len is None else int(x.kv_len[0])
-        rec["cpu_baseline"] = cpu_baseline(x, allowed_pairs(wl.N, wl.causal, x.blockmask, kv0))
+        rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
 
 

@@ -76,10 +76,13 @@ def rel_l2(a, b):
     return np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
 
 
-def check_o(o, ref, what=""):
+def check_o(o, ref, what="", rel_slack=0.0):
+    """max |o - ref| <= 1e-2 (+ rel_slack * |ref| elementwise, for stress inputs whose
+    outputs exceed the range the 1e-2 bound was set for), and relative L2 <= 5e-3."""
     err = np.abs(o - ref).max() if o.size else 0.0
+    bound = O_MAX_ABS + rel_slack * np.abs(ref)
     rl = rel_l2(o, ref)
-    assert err <= O_MAX_ABS, f"{what} O max-abs {err:.3e}"
+    assert (np.abs(o - ref) <= bound).all(), f"{what} O max-abs {err:.3e}"
     assert rl <= O_REL_L2, f"{what} O rel-L2 {rl:.3e}"
     return err, rl
 
@@ -106,9 +109,9 @@ def check_grad(g, ref, name, what=""):
     return rl
 
 
-def check_all(res, ref, what="", grads=True):
+def check_all(res, ref, what="", grads=True, o_rel_slack=0.0):
     out = {}
-    out["O"] = check_o(res["O"], ref["O"], what)
+    out["O"] = check_o(res["O"], ref["O"], what, o_rel_slack)
     out["LSE"] = check_lse(res["LSE"], ref["LSE"], what)
     if grads:
         for name in ("dQ", "dK", "dV"):

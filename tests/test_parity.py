@@ -22,11 +22,12 @@ def oracle_all(q, k, v, do, scale, causal=False, bm=None, kv=None):
     return orc.backward(q, k, v, do, scale, causal, bm, kv)
 
 
-def run_and_check(q, k, v, do, scale, causal=False, bm=None, kv=None, what=""):
+def run_and_check(q, k, v, do, scale, causal=False, bm=None, kv=None, what="",
+                  o_rel_slack=0.0):
     say(f"[parity] {what} shape={q.shape} causal={causal} bm={bm is not None} kv={kv}")
     res = Run(q, k, v, do, scale, causal, bm, kv).result()
     ref = oracle_all(q, k, v, do, scale, causal, bm, kv)
-    check_all(res, ref, what)
+    check_all(res, ref, what, o_rel_slack=o_rel_slack)
     return res, ref
 
 
@@ -80,12 +81,22 @@ def test_all_masks_together(d):
     run_and_check(q, k, v, do, 0.09, True, bm=bm, kv=kv, what=f"all masks d={d}")
 
 
+# Scores ~9x wider than the workloads' make P nearly one-hot, so |O| reaches |V| (up to
+# ~4.5); O is returned in bf16, whose rounding alone is 2^-9 relative (0.0156 at |O| = 4+),
+# and P enters the P.V product in bf16 (another 2^-9 relative). The max-abs bound gets that
+# 2^-8 |O| slack here; the relative L2 and gradient bounds are unchanged.
+WIDE_SLACK = 2.0 ** -8
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_negative_scale_and_wide_scores(d):
     N = 200
     q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=17, dist="wide")
-    run_and_check(q, k, v, do, -0.2, False, what=f"negative scale d={d}")
-    run_and_check(q, k, v, do, 0.2, True, what=f"wide causal d={d}")
+    run_and_check(q, k, v, do, -0.2, False, what=f"negative scale d={d}",
+                  o_rel_slack=WIDE_SLACK)
+    run_and_check(q, k, v, do, 0.2, True, what=f"wide causal d={d}", o_rel_slack=WIDE_SLACK)
+    q1, k1, v1, do1 = inp.custom_inputs(1, 2, N, d, seed=18)
+    run_and_check(q1, k1, v1, do1, -0.125, True, what=f"negative scale N(0,1) d={d}")
 
 
 # ------------------------------------------------------- closed forms on GPU
