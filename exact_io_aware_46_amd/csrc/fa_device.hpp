@@ -100,4 +100,48 @@ __device__ __forceinline__ u32x2 transpose_col(const u32x4 (&rows)[4], int e) {
 // all banks.
 __device__ __forceinline__ int tchunk(int row, int chunk) { return chunk ^ ((row >> 4) & 7); }
 
+// ---------------------------------------------------------------------------------
+// Row-major tiles in LDS with 16-byte chunks XOR-swizzled by row.
+//
+// A tile row holds CH 16-byte chunks (CH = d / 8). Logical chunk c of row k is stored at
+// physical chunk c ^ swz<CH>(k). The swizzle is a permutation of the low row bits chosen
+// so that (a) the 16 rows read by one 16-lane phase of a row-major MFMA operand load hit
+// 16 different bank groups, and (b) the rows read by one LDS transpose load spread too.
+template <int CH>
+__device__ __forceinline__ int swz(int k) {
+  if constexpr (CH == 16) return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8);
+  else return (((k >> 1) & 3) << 1) | ((k >> 3) & 1);
+}
+
+// Byte offset of element `col` (a multiple of 4) of row `row` in a swizzled tile.
+template <int CH>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * (CH * 16) + (((col >> 3) ^ swz<CH>(row)) << 4) + ((col & 7) << 1);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane: lane l's word lands at lds_base + 4 * l.
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// LDS transpose load (8 bytes per lane). Within each group of 16 lanes, output lane i
+// receives, as element r (r = 0..3), the (i % 4)-th 16-bit value of the 8 bytes that lane
+// 4r + i/4 of the group addressed. Used to read a row-major tile as the contraction-major
+// MFMA operand: lane 4r + q addresses row r, columns c0 + 4q .. c0 + 4q + 3, so lane i
+// gets column c0 + i of rows 0..3.
+__device__ __forceinline__ i16x4 lds_tr4(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds_ptr);
+}
+
 }  // namespace fa

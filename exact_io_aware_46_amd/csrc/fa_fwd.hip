@@ -14,11 +14,14 @@
 //
 // gfx950 mapping:
 //   workgroup = 4 waves = 128 queries of one (b, h); wave w owns queries 32w .. 32w+31.
-//   Each key tile (BC keys) is staged in LDS: K row-major, V transposed (d-major).
+//   Key tiles (BC keys) of K and V are copied HBM -> LDS by the DMA path of the vector
+//   memory unit (global_load_lds, no registers), double-buffered so the next tile streams
+//   in while the current one is used, and kept row-major with XOR-swizzled 16-byte chunks.
 //   The score tile is computed transposed, S^T = K Q^T, with MFMA 32x32x16 (bf16 -> fp32):
 //   lane l then holds scores of query (l % 32) only, so the row maximum is an in-lane
 //   reduction plus one cross-half permlane swap, and the exponentiated tile is already in
-//   the register layout of the B operand of O^T += V^T P^T (no LDS round trip for P).
+//   the register layout of the B operand of O^T += V^T P^T (no LDS round trip for P);
+//   the V^T operand is read from the row-major tile with LDS transpose loads.
 //   Q stays in registers for the whole workgroup; O^T accumulates in registers.
 #include "fa_device.hpp"
 #include "fa_internal.h"
@@ -28,14 +31,16 @@ namespace {
 
 template <int D, int BC>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  constexpr int BR = 128;      // queries per workgroup
-  constexpr int NS = D / 16;   // contraction steps of the score MFMA
-  constexpr int KB = BC / 32;  // 32-key blocks per key tile
-  constexpr int DB = D / 32;   // 32-wide column blocks of O
-  constexpr int KP = D + 8;    // K tile pitch (elements)
-  constexpr int VP = BC + 8;   // V^T tile pitch (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VP];
+  constexpr int BR = 128;           // queries per workgroup
+  constexpr int NS = D / 16;        // contraction steps of the score MFMA
+  constexpr int KB = BC / 32;       // 32-key blocks per key tile
+  constexpr int DB = D / 32;        // 32-wide column blocks of O
+  constexpr int CH = D / 8;         // 16-byte chunks per row
+  constexpr int ROWB = D * 2;       // bytes per row
+  constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
+  constexpr int LPW = TILE / 1024 / 4;  // 1 KB wave-wide DMA loads per wave per tile
+  // Two stages (double buffering) of a K tile and a V tile, both row-major, swizzled.
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -50,6 +55,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int grp = lane >> 4;  // 16-lane group (transpose loads)
+  const int t16 = lane & 15;
 
   const size_t hoff = (size_t)bh * N * D;
   const uint16_t* __restrict__ Q = p.q + hoff;
@@ -66,11 +73,38 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (p.causal) kend = min(kend, q0 + BR);
   const int nkt = (kend + BC - 1) / BC;
   const int nb = (N + 127) >> 7;
+  const uint8_t* bmrow = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+
+  // Next key tile at or after kt that the block table keeps (all of them without one).
+  auto next_tile = [&](int kt) {
+    if (bmrow)
+      while (kt < nkt && !bmrow[(kt * BC) >> 7]) ++kt;
+    return kt;
+  };
+  // Asynchronous copy of key tile kt into a stage: every lane moves 16 bytes straight
+  // from HBM into LDS. Rows at or past klim fetch row klim-1 instead (they are masked,
+  // and reading a valid row keeps every access in bounds).
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * BC;
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const int g = wave * LPW + t;
+      const int byte = g * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
+      g2lds16(K + goff, &smem[stage][0][g * 1024]);
+      g2lds16(V + goff, &smem[stage][1][g * 1024]);
+    }
+  };
 
   // A negative scale is folded into Q (bf16 negation is exact), so the exponent scale is
   // positive and the row maximum can be taken on raw scores.
   const float sc = fabsf(p.scale) * kLog2e;
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+
+  int kt = next_tile(0);
+  if (kt < nkt) issue(kt, 0);
 
   bf16x8 qf[NS];
 #pragma unroll
@@ -84,53 +118,36 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   f32x16 acc[DB];
 #pragma unroll
   for (int j = 0; j < DB; ++j) acc[j] = zero16();
-  float m_run = -kInf;  // running max of scale*log2(e)*S for this lane's query
-  float l_run = 0.f;    // running sum of exp2(.) over this lane's half of the keys
+  // Reference max (log2 units, scale folded in) of this lane's query and the running sum
+  // of exp2(score - reference) over this lane's half of the keys. The reference is only
+  // raised when a tile's max exceeds it by more than 8 (a factor 256), which keeps every
+  // exponent <= 2^8 and skips most rescalings of O; the result is the same softmax.
+  float m_run = -kInf;
+  float l_run = 0.f;
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  int stage = 0;
+  while (kt < nkt) {
+    wait_vm0();       // this stage's copies have landed ...
+    __syncthreads();  // ... for every wave, and the other stage is free again
+    const int ktn = next_tile(kt + 1);
+    if (ktn < nkt) issue(ktn, stage ^ 1);
+
     const int k0 = kt * BC;
-    if (p.blockmask && !p.blockmask[(q0 >> 7) * nb + (k0 >> 7)]) continue;
-
-    __syncthreads();  // the previous tile is no longer being read
-    // K tile, row-major. Keys at or past klim are stored as zeros, so no masked value
-    // (not even a NaN) can reach the MFMAs.
-#pragma unroll
-    for (int c = tid; c < BC * D / 8; c += 256) {
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (k0 + r < klim) x = ldg16(K + (size_t)(k0 + r) * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(&sK[r * KP + c8 * 8]) = x;
-    }
-    // V tile, transposed: sV[d][key] (16-byte chunks XOR-swizzled by row).
-#pragma unroll
-    for (int u = tid; u < (BC / 4) * (D / 8); u += 256) {
-      const int kg = u / (D / 8), dc = u % (D / 8);
-      u32x4 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * kg + r;
-        rows[r] = u32x4{0u, 0u, 0u, 0u};
-        if (key < klim) rows[r] = ldg16(V + (size_t)key * D + dc * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = dc * 8 + e;
-        const int col = tchunk(row, kg >> 1) * 8 + (kg & 1) * 4;
-        *reinterpret_cast<u32x2*>(&sV[row * VP + col]) = transpose_col(rows, e);
-      }
-    }
-    __syncthreads();
-
+    const char* sK = smem[stage][0];
+    const char* sV = smem[stage][1];
+    kt = ktn;
+    stage ^= 1;
     if (qw >= N || (p.causal && k0 > qw + 31)) continue;  // nothing allowed for this wave
 
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
-      const uint16_t* krow = &sK[(kb * 32 + perm_row(l32)) * KP + 8 * hi];
+      const int row = kb * 32 + perm_row(l32);
 #pragma unroll
       for (int st = 0; st < NS; ++st)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st), qf[st], s[kb]);
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sK + swz_off<CH>(row, 16 * st + 8 * hi)),
+                       qf[st], s[kb]);
     }
 
     if ((p.causal && k0 + BC - 1 > qw) || k0 + BC > klim) {
@@ -149,11 +166,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx * sc);
-    const float m_use = m_new == -kInf ? 0.f : m_new;  // all keys masked so far
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    mx = xhalf_max(mx) * sc;
+    const bool up = mx > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mx : m_run;
+      const float alpha = up ? fast_exp2(m_run - m_new) : 1.f;  // m_run = -inf -> 0
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < DB; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[j][i] *= alpha;
+    }
+    const float m_use = m_run == -kInf ? 0.f : m_run;  // all keys masked so far
 
     float lsum = 0.f;
 #pragma unroll
@@ -164,23 +189,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         s[kb][i] = e;
         lsum += e;
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int j = 0; j < DB; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[j][i] *= alpha;
+    l_run += lsum;
 
+    // O^T += V^T P^T. V^T comes from the row-major V tile through transpose loads: lane
+    // t of 16-lane group g reads keys (8*(g/2) + t/4) and (+4), columns 16*(g%2) + 4*(t%4).
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const bf16x8 pf = pack8(s[kb], 8 * half);
-        const int chunk = (kb * 32 + 16 * half + 8 * hi) >> 3;
+        const int row0 = kb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
-          const int row = j * 32 + l32;
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(&sV[row * VP + tchunk(row, chunk) * 8]);
+          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
+          const i16x4 a0 = lds_tr4(sV + swz_off<CH>(row0, col));
+          const i16x4 a1 = lds_tr4(sV + swz_off<CH>(row0 + 4, col));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, (i16x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
           acc[j] = mfma32(vf, pf, acc[j]);
         }
       }
