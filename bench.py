@@ -259,13 +259,15 @@ def main():
         "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_bwd_pct_mfma_peak": round(100 * tf_step / MFMA_BF16_PEAK_TFLOPS, 2),
         "bwd_ms": round(ms_bwd, 4), "bwd_preprocess_ms": round(ms_pre, 4),
-        "roofline": {"kernel": f"bwd_kernel<{wl.d}> + dq_convert (fa_bwd_ex minus "
-                               "fa_bwd_preprocess)",
+        "roofline": {"kernel": f"bwd_dkdv_kernel<{wl.d}> + bwd_dq_kernel<{wl.d}> "
+                               "(fa_bwd_ex minus fa_bwd_preprocess)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(wl.name, "bwd_kernel",
-                                                 [f"bwd_kernel<{wl.d}>", "dq_convert_kernel"])},
+                     "traffic": measured_traffic(
+                         wl.name, "bwd_kernel",
+                         [f"bwd_dkdv_kernel<{wl.d}>",
+                          f"bwd_dq_kernel<{wl.d}, 64>"])},
         "roofline_fwd": {"kernel": f"fwd_kernel<{wl.d}>", "bound": "mfma",
                          "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -104,7 +104,7 @@ int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, 
   const size_t tbytes = (size_t)B * H * N * d * 2;
   const Range rd = span(delta, (size_t)B * H * N * 4);
   if (overlap(rd, span(o, tbytes)) || overlap(rd, span(dO, tbytes))) return FA_ERR_ALIAS;
-  if (fa::launch_bwd_preprocess(o, dO, delta, nullptr, B * H * N, d,
+  if (fa::launch_bwd_preprocess(o, dO, nullptr, delta, nullptr, B * H * N, d,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
@@ -113,7 +113,7 @@ int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d) != FA_OK) return 0;
   const size_t rows = (size_t)B * H * N;
-  return round_up(rows * 4, kWsAlign) + rows * (size_t)d * 4;
+  return 2 * round_up(rows * 4, kWsAlign);
 }
 
 int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
@@ -148,7 +148,7 @@ int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf1
   p.blockmask = blockmask;
   p.kv_len = kv_len;
   p.delta = reinterpret_cast<float*>(ws);
-  p.dq_accum = reinterpret_cast<float*>(ws + round_up(rows * 4, kWsAlign));
+  p.lse2 = reinterpret_cast<float*>(ws + round_up(rows * 4, kWsAlign));
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;
   p.causal = causal ? 1 : 0;

@@ -1,26 +1,26 @@
-// Backward kernels: D = rowsum(dO * O); then dQ, dK, dV with P recomputed from LSE.
+// Backward kernels: D = rowsum(dO * O); then dK, dV and dQ with P recomputed from LSE.
 //
 // Recomputing the attention matrix in backward from the per-row statistic saved by the
 // forward, instead of storing it, is the report's third algorithm bullet (report on
 // "FlashAttention：一种基于I/O感知的快速且内存高效的自注意力算法", fmread.com, section 算法设计;
 // also the 中文速览 of "FlashAttention: Fast and Memory-Efficient Exact Attention with
-// IO-Awareness", aha.fim.ai). The loop order -- key/value blocks outer, query blocks
-// inner -- is the one drawn on "FlashAttention学习笔记" (amentiraz.github.io), section
-// 分块计算整体流程(Tiling): dK and dV of a key block stay in registers for the whole pass.
-// The gradient equations are the textbook ones for O = softmax(scale*QK^T + mask) V and
-// are not printed on the pages:
+// IO-Awareness", aha.fim.ai). The key/value-outer loop order drawn on "FlashAttention学习笔记"
+// (amentiraz.github.io), section 分块计算整体流程(Tiling), is used for dK and dV, which then
+// stay in registers for a whole pass over the queries. The gradient equations are the
+// textbook ones for O = softmax(scale*QK^T + mask) V and are not printed on the pages:
 //   P = exp(scale*S - LSE), dV = P^T dO, dP = dO V^T, dS = P * (dP - D),
 //   dQ = scale * dS K, dK = scale * dS^T Q.
 //
-// gfx950 mapping (workgroup = 4 waves = 128 keys of one (b, h); wave w owns 32 keys):
-//   K and V rows of the wave live in registers as MFMA operands; K^T of the whole tile is
-//   staged once in LDS for the dQ product.
-//   Per 64-query tile: Q and dO are staged in LDS both row-major (score / dP operands) and
-//   transposed (dK / dV operands). S and dP are computed in [query][key] orientation, so
-//   lane l holds key (l % 32) and the exponentiated tile is directly the A operand of
-//   dV += P^T dO and dK += dS^T Q. dS goes through LDS once, row-major, for
-//   dQ = dS K over all 128 keys of the workgroup, added to a fp32 accumulator with
-//   global atomics. A last kernel scales and rounds the accumulator into dQ.
+// dQ is a sum over key tiles. Accumulating it from the key-outer pass would need one fp32
+// atomic per (key tile, query, column): 8.7 GB for 16 heads of 16K causal queries at
+// d = 128, and memory-side atomics on this part sustain only ~1.3 TB/s. Instead a second,
+// query-outer pass recomputes S and dP per tile and accumulates dQ in registers (three
+// MFMA products instead of one, no atomics, and dQ is deterministic).
+//
+// gfx950 mapping shared by both passes: 4 waves per workgroup, each owning 32 rows of
+// the outer dimension; inner tiles are copied HBM -> LDS by global_load_lds (no
+// registers), double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that
+// must be contraction-major are read with LDS transpose loads.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -29,12 +29,14 @@ namespace {
 
 // ---------------------------------------------------------------- preprocess
 
+// Per row: delta = sum_c dO*O (fp32); optionally lse2 = LSE*log2(e) with a fully masked
+// row (LSE = -inf) mapped to +inf, so exp2(s - lse2) = 0 needs no test in the main passes.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ lse,
                                                       float* __restrict__ delta,
-                                                      float* __restrict__ dq_accum,
-                                                      int rows) {
+                                                      float* __restrict__ lse2, int rows) {
   constexpr int TPR = D / 8;        // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;    // rows per block
   const int tid = threadIdx.x;
@@ -49,57 +51,41 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       acc += __uint_as_float(a[w] << 16) * __uint_as_float(g[w] << 16);
       acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(g[w] & 0xffff0000u);
     }
-    if (dq_accum) {
-      float4* z = reinterpret_cast<float4*>(dq_accum + row * D + c * 8);
-      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
 #pragma unroll
   for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
-  if (row < rows && c == 0) delta[row] = acc;
-}
-
-// ------------------------------------------------------------ dQ finalisation
-
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
-                                                         uint16_t* __restrict__ dq, long n8,
-                                                         float scale) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
-    const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-    const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-    u32x4 r;
-    r[0] = pack_bf16(a.x * scale, a.y * scale);
-    r[1] = pack_bf16(a.z * scale, a.w * scale);
-    r[2] = pack_bf16(b.x * scale, b.y * scale);
-    r[3] = pack_bf16(b.z * scale, b.w * scale);
-    reinterpret_cast<u32x4*>(dq)[i] = r;
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    if (lse2) {
+      const float l = lse[row];
+      lse2[row] = l == -kInf ? kInf : l * kLog2e;
+    }
   }
 }
 
-// ------------------------------------------------------------------ main pass
+// ------------------------------------------------------------- dK, dV pass
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
-  constexpr int BKC = 128;    // keys per workgroup
-  constexpr int BQ = 64;      // queries per inner step
-  constexpr int NS = D / 16;  // contraction steps over d
-  constexpr int DB = D / 32;  // 32-wide column blocks over d
-  constexpr int QP = D + 8;   // row-major Q / dO pitch
-  constexpr int TP = BQ + 8;  // transposed Q / dO pitch
-  constexpr int KTP = BKC + 8;
-  constexpr int SP = BKC + 8;
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BKC = 128;           // keys per workgroup (4 waves x 32)
+  constexpr int BQ = 64;             // queries per inner step
+  constexpr int NS = D / 16;         // contraction steps over d
+  constexpr int DB = D / 32;         // 32-wide column blocks over d
+  constexpr int CH = D / 8;          // 16-byte chunks per row of Q, dO
+  constexpr int ROWB = D * 2;
   constexpr int NQB = BQ / 32;
-  constexpr int DQ_BLOCKS = NQB * DB;      // 32x32 blocks of the dQ tile
-  constexpr int DQ_PER_WAVE = DQ_BLOCKS / 4;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * KTP];
-  __shared__ __attribute__((aligned(16))) uint16_t sdS[BQ * SP];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[BQ];
+  constexpr int QTILE = BQ * ROWB;   // bytes of one Q (or dO) tile
+  constexpr int QLPW = QTILE / 4096; // 1 KB DMA loads per wave per Q tile
+  // Every stage is its own array so the compiler can tell the tiles being read from the
+  // ones being filled by in-flight copies, and does not wait for those before reading.
+  __shared__ __attribute__((aligned(1024))) char sQ0[QTILE];
+  __shared__ __attribute__((aligned(1024))) char sQ1[QTILE];
+  __shared__ __attribute__((aligned(1024))) char sdO0[QTILE];
+  __shared__ __attribute__((aligned(1024))) char sdO1[QTILE];
+  __shared__ __attribute__((aligned(256))) float sL0[BQ];
+  __shared__ __attribute__((aligned(256))) float sL1[BQ];
+  __shared__ __attribute__((aligned(256))) float sD0[BQ];
+  __shared__ __attribute__((aligned(256))) float sD1[BQ];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -111,15 +97,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int grp = lane >> 4;
+  const int t16 = lane & 15;
 
   const size_t hoff = (size_t)bh * N * D;
   const uint16_t* __restrict__ Q = p.q + hoff;
   const uint16_t* __restrict__ K = p.k + hoff;
   const uint16_t* __restrict__ V = p.v + hoff;
   const uint16_t* __restrict__ dO = p.dO + hoff;
-  const float* __restrict__ LSE = p.lse + (size_t)bh * N;
+  const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
   const float* __restrict__ DL = p.delta + (size_t)bh * N;
-  float* __restrict__ dQacc = p.dq_accum + hoff;
 
   const int k0 = kt * BKC;
   const int kw = k0 + wave * 32;
@@ -128,38 +115,53 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
   const int nb = (N + 127) >> 7;
 
+  // A negative scale is folded into this wave's K registers (used only for S); dK takes
+  // the signed scale at the end.
   const float sc = fabsf(p.scale) * kLog2e;
-  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+  const uint32_t ksign = p.scale < 0.f ? 0x80008000u : 0u;
 
-  // This wave's K and V rows as B operands of S = Q K^T and dP = dO V^T.
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt_begin = p.causal ? k0 / BQ : 0;
+  const int qt_end = k0 < klim ? nqt : qt_begin;  // a fully padded key tile gets no work
+
+  auto next_q = [&](int qt) {
+    if (p.blockmask)
+      while (qt < qt_end && !p.blockmask[(size_t)((qt * BQ) >> 7) * nb + (k0 >> 7)]) ++qt;
+    return qt;
+  };
+  // Query tile qt -> stage: Q and dO rows (row-major, swizzled), log2-scaled LSE and D.
+  // Rows past N fetch row N-1 (masked later; keeps every access in bounds).
+  auto issue_q = [&](int qt, char* dQs, char* ddO, float* dL, float* dD) {
+    const int q0 = qt * BQ;
+#pragma unroll
+    for (int t = 0; t < QLPW; ++t) {
+      const int g = wave * QLPW + t;
+      const int byte = g * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
+      const size_t goff = (size_t)min(q0 + row, N - 1) * D + lch * 8;
+      g2lds16(Q + goff, dQs + g * 1024);
+      g2lds16(dO + goff, ddO + g * 1024);
+    }
+    if (wave == 0) g2lds4(L2 + min(q0 + lane, N - 1), dL);
+    if (wave == 1) g2lds4(DL + min(q0 + lane, N - 1), dD);
+  };
+
+  int qt = next_q(qt_begin);
+  if (qt < qt_end) issue_q(qt, sQ0, sdO0, sL0, sD0);
+
+  // This wave's K and V rows as B operands of S = Q K^T and dP = dO V^T (zeros past klim).
   bf16x8 kreg[NS], vreg[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (mykey < klim) {  // masked keys are zeros
+    if (mykey < klim) {
       x = ldg16(K + (size_t)mykey * D + 16 * s + 8 * hi);
       y = ldg16(V + (size_t)mykey * D + 16 * s + 8 * hi);
     }
+    x[0] ^= ksign; x[1] ^= ksign; x[2] ^= ksign; x[3] ^= ksign;
     kreg[s] = as_bf16x8(x);
     vreg[s] = as_bf16x8(y);
-  }
-  // K^T of the whole key tile for dQ = dS K.
-#pragma unroll
-  for (int u = tid; u < (BKC / 4) * (D / 8); u += 256) {
-    const int kg = u / (D / 8), dc = u % (D / 8);
-    u32x4 rows[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * kg + r;
-      rows[r] = u32x4{0u, 0u, 0u, 0u};
-      if (key < klim) rows[r] = ldg16(K + (size_t)key * D + dc * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = dc * 8 + e;
-      *reinterpret_cast<u32x2*>(&sKt[row * KTP + tchunk(row, kg >> 1) * 8 + (kg & 1) * 4]) =
-          transpose_col(rows, e);
-    }
   }
 
   f32x16 acc_dk[DB], acc_dv[DB];
@@ -169,152 +171,86 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     acc_dv[j] = zero16();
   }
 
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt_begin = p.causal ? k0 / BQ : 0;
-  const int qt_end = k0 < klim ? nqt : qt_begin;  // a fully padded key tile gets no work
-
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
+  // One query tile against this wave's keys: S and dP (MFMA, [query][key] orientation, so
+  // lane l holds key l%32), P and dS in fp32, then dV += P^T dO and dK += dS^T Q with the
+  // exponentiated tiles as A operands straight from registers and dO^T, Q^T read from the
+  // row-major tiles by transpose loads.
+  auto step = [&](int qt, const char* Qs, const char* dOs, const float* Ls, const float* Ds) {
     const int q0 = qt * BQ;
-    if (p.blockmask && !p.blockmask[(q0 >> 7) * nb + (k0 >> 7)]) continue;
-
-    __syncthreads();  // previous step's LDS reads are done
-    // Q and dO tiles: each unit is 4 rows x 8 columns, written row-major and transposed.
+    if ((p.causal && kw > q0 + BQ - 1) || kw >= klim) return;  // nothing allowed here
+    f32x16 s[NQB], dp[NQB];
 #pragma unroll
-    for (int u = tid; u < 2 * (BQ / 4) * (D / 8); u += 256) {
-      const bool isq = u < (BQ / 4) * (D / 8);
-      const int uu = isq ? u : u - (BQ / 4) * (D / 8);
-      const int rg = uu / (D / 8), dc = uu % (D / 8);
-      const uint16_t* src = isq ? Q : dO;
-      const uint32_t sgn = isq ? qsign : 0u;
-      u32x4 rows[4];
+    for (int qb = 0; qb < NQB; ++qb) {
+      s[qb] = zero16();
+      dp[qb] = zero16();
+      const int row = qb * 32 + perm_row(l32);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = q0 + 4 * rg + r;
-        rows[r] = u32x4{0u, 0u, 0u, 0u};
-        if (q < N) {
-          rows[r] = ldg16(src + (size_t)q * D + dc * 8);
-          rows[r][0] ^= sgn; rows[r][1] ^= sgn; rows[r][2] ^= sgn; rows[r][3] ^= sgn;
-        }
-      }
-      uint16_t* nat = isq ? sQ : sdO;
-      uint16_t* tr = isq ? sQt : sdOt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u32x4*>(&nat[(4 * rg + r) * QP + dc * 8]) = rows[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = dc * 8 + e;
-        *reinterpret_cast<u32x2*>(&tr[row * TP + tchunk(row, rg >> 1) * 8 + (rg & 1) * 4]) =
-            transpose_col(rows, e);
+      for (int k = 0; k < NS; ++k) {
+        const int off = swz_off<CH>(row, 16 * k + 8 * hi);
+        s[qb] = mfma32(*reinterpret_cast<const bf16x8*>(Qs + off), kreg[k], s[qb]);
+        dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dOs + off), vreg[k], dp[qb]);
       }
     }
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      float l = kInf, dl = 0.f;  // rows past N: exp2(x - inf) = 0
-      if (q < N) {
-        const float lse = LSE[q];
-        l = lse == -kInf ? kInf : lse * kLog2e;  // fully masked row: P = 0
-        dl = DL[q];
-      }
-      sL[tid] = l;
-      sDl[tid] = dl;
-    }
-    __syncthreads();
-
-    const bool active = !(p.causal && kw > q0 + BQ - 1) && kw < klim;
-    if (active) {
-      f32x16 s[NQB], dp[NQB];
+    const bool need_mask = (p.causal && kw + 31 > q0) || kw + 32 > klim || q0 + BQ > N;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        s[qb] = zero16();
-        dp[qb] = zero16();
-        const int r = (qb * 32 + perm_row(l32)) * QP + 8 * hi;
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s[qb] = mfma32(*reinterpret_cast<const bf16x8*>(&sQ[r + 16 * st]), kreg[st], s[qb]);
-          dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(&sdO[r + 16 * st]), vreg[st], dp[qb]);
-        }
-      }
-      const bool need_mask = (p.causal && kw + 31 > q0) || kw + 32 > klim;
+      for (int half = 0; half < 2; ++half) {
+        const int qloc = qb * 32 + 16 * half + 8 * hi;
+        const float4 la = *reinterpret_cast<const float4*>(&Ls[qloc]);
+        const float4 lb = *reinterpret_cast<const float4*>(&Ls[qloc + 4]);
+        const float4 da = *reinterpret_cast<const float4*>(&Ds[qloc]);
+        const float4 db = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
+        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int qloc = qb * 32 + 16 * half + 8 * hi;
-          const float4 la = *reinterpret_cast<const float4*>(&sL[qloc]);
-          const float4 lb = *reinterpret_cast<const float4*>(&sL[qloc + 4]);
-          const float4 da = *reinterpret_cast<const float4*>(&sDl[qloc]);
-          const float4 db = *reinterpret_cast<const float4*>(&sDl[qloc + 4]);
-          const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-          const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * half + j;
-            float pv = fast_exp2(s[qb][i] * sc - lv[j]);
-            if (need_mask) {
-              const int q = q0 + qloc + j;
-              const bool ok = mykey < klim && (!p.causal || mykey <= q);
-              if (!ok) pv = 0.f;
-            }
-            s[qb][i] = pv;
-            dp[qb][i] = pv * (dp[qb][i] - dv[j]);
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * half + j;
+          float pv = fast_exp2(s[qb][i] * sc - lv[j]);
+          if (need_mask) {
+            const int q = q0 + qloc + j;
+            const bool ok = mykey < klim && (!p.causal || mykey <= q) && q < N;
+            if (!ok) pv = 0.f;
           }
+          s[qb][i] = pv;
+          dp[qb][i] = pv * (dp[qb][i] - dv[j]);
         }
-      // dV += P^T dO and dK += dS^T Q (contraction over the 64 queries).
+      }
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 pa = pack8(s[qb], 8 * half);
-          const bf16x8 da = pack8(dp[qb], 8 * half);
-          const int chunk = (qb * 32 + 16 * half + 8 * hi) >> 3;
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 pa = pack8(s[qb], 8 * half);
+        const bf16x8 da = pack8(dp[qb], 8 * half);
+        const int row0 = qb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
 #pragma unroll
-          for (int j = 0; j < DB; ++j) {
-            const int row = j * 32 + l32;
-            const int off = row * TP + tchunk(row, chunk) * 8;
-            acc_dv[j] = mfma32(pa, *reinterpret_cast<const bf16x8*>(&sdOt[off]), acc_dv[j]);
-            acc_dk[j] = mfma32(da, *reinterpret_cast<const bf16x8*>(&sQt[off]), acc_dk[j]);
-          }
+        for (int j = 0; j < DB; ++j) {
+          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
+          const int o0 = swz_off<CH>(row0, col), o1 = swz_off<CH>(row0 + 4, col);
+          acc_dv[j] = mfma32(pa, cat_tr(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
+          acc_dk[j] = mfma32(da, cat_tr(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
         }
-      // dS (bf16) into LDS, row-major [query][key].
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sdS[(qb * 32 + acc_row(i, hi)) * SP + wave * 32 + l32] = (uint16_t)bf16_bits(dp[qb][i]);
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sdS[(qb * 32 + acc_row(i, hi)) * SP + wave * 32 + l32] = 0;
-    }
-    __syncthreads();
+      }
+  };
 
-    // dQ tile partial: [64 queries][D] = dS [64][128 keys] K [128][D], atomically added.
-#pragma unroll
-    for (int x = 0; x < DQ_PER_WAVE; ++x) {
-      const int blk = wave * DQ_PER_WAVE + x;
-      const int qb = blk / DB, j = blk % DB;
-      f32x16 acc = zero16();
-      const int arow = (qb * 32 + l32) * SP + 8 * hi;
-      const int brow = j * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < BKC / 16; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdS[arow + 16 * t]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(
-            &sKt[brow * KTP + tchunk(brow, 2 * t + hi) * 8]);
-        acc = mfma32(a, bk, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (q < N) unsafeAtomicAdd(&dQacc[(size_t)q * D + j * 32 + l32], acc[i]);
-      }
-    }
+  // Main loop over pairs of query tiles (stage 0, then stage 1), one back-edge, so each
+  // half reads fixed stages while the other fills.
+  while (qt < qt_end) {
+    wait_vm0();
+    __syncthreads();  // stage 0 has landed everywhere; stage 1 is free
+    const int qb = next_q(qt + 1);
+    if (qb < qt_end) issue_q(qb, sQ1, sdO1, sL1, sD1);
+    step(qt, sQ0, sdO0, sL0, sD0);
+
+    wait_vm0();
+    __syncthreads();  // stage 1 has landed; stage 0 is free
+    const int qc = qb < qt_end ? next_q(qb + 1) : qt_end;
+    if (qc < qt_end) issue_q(qc, sQ0, sdO0, sL0, sD0);
+    if (qb < qt_end) step(qb, sQ1, sdO1, sL1, sD1);
+    qt = qc;
   }
 
-  // Epilogue: dK = |scale| * acc_dk (Q was sign-adjusted), dV = acc_dv.
-  const float ks = fabsf(p.scale);
+  // Epilogue: dK = scale * acc_dk (K's sign was only folded into S), dV = acc_dv.
 #pragma unroll
   for (int j = 0; j < DB; ++j)
 #pragma unroll
@@ -322,44 +258,217 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
       if (key < N) {
         const size_t off = hoff + (size_t)key * D + j * 32 + l32;
-        p.dk[off] = (uint16_t)bf16_bits(acc_dk[j][i] * ks);
+        p.dk[off] = (uint16_t)bf16_bits(acc_dk[j][i] * p.scale);
         p.dv[off] = (uint16_t)bf16_bits(acc_dv[j][i]);
       }
     }
 }
 
+// ----------------------------------------------------------------- dQ pass
+
+template <int D, int BC>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BR = 128;           // queries per workgroup
+  constexpr int NS = D / 16;
+  constexpr int KB = BC / 32;
+  constexpr int DB = D / 32;
+  constexpr int CH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = BC * ROWB;
+  constexpr int LPW = TILE / 4096;
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILE];
+
+  const int N = p.N;
+  const int BH = p.B * p.H;
+  const int nqt = (N + BR - 1) / BR;
+  const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest (causal) tiles first
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / p.H;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int grp = lane >> 4;
+  const int t16 = lane & 15;
+
+  const size_t hoff = (size_t)bh * N * D;
+  const uint16_t* __restrict__ Q = p.q + hoff;
+  const uint16_t* __restrict__ K = p.k + hoff;
+  const uint16_t* __restrict__ V = p.v + hoff;
+  const uint16_t* __restrict__ dO = p.dO + hoff;
+
+  const int q0 = qt * BR;
+  const int qw = q0 + wave * 32;
+  const int myq = qw + l32;
+
+  int klim = N;
+  if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
+  int kend = klim;
+  if (p.causal) kend = min(kend, q0 + BR);
+  const int nkt = (kend + BC - 1) / BC;
+  const int nb = (N + 127) >> 7;
+  const uint8_t* bmrow = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+
+  auto next_tile = [&](int kt) {
+    if (bmrow)
+      while (kt < nkt && !bmrow[(kt * BC) >> 7]) ++kt;
+    return kt;
+  };
+  // Key tile kt -> stage (K and V rows; rows at or past klim fetch row klim-1, masked).
+  auto issue = [&](int kt, char* dK, char* dV) {
+    const int k0 = kt * BC;
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const int g = wave * LPW + t;
+      const int byte = g * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
+      g2lds16(K + goff, dK + g * 1024);
+      g2lds16(V + goff, dV + g * 1024);
+    }
+  };
+
+  const float sc = fabsf(p.scale) * kLog2e;
+  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+
+  int kt = next_tile(0);
+  if (kt < nkt) issue(kt, sK0, sV0);
+
+  // This lane's query row of Q (sign-adjusted) and dO, as B operands of S^T = K Q^T and
+  // dP^T = V dO^T; its log2-scaled LSE and D.
+  bf16x8 qf[NS], gf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (myq < N) {
+      x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
+      y = ldg16(dO + (size_t)myq * D + 16 * s + 8 * hi);
+    }
+    x[0] ^= qsign; x[1] ^= qsign; x[2] ^= qsign; x[3] ^= qsign;
+    qf[s] = as_bf16x8(x);
+    gf[s] = as_bf16x8(y);
+  }
+  const float lq = myq < N ? p.lse2[(size_t)bh * N + myq] : kInf;  // +inf: P = 0
+  const float dlq = myq < N ? p.delta[(size_t)bh * N + myq] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int j = 0; j < DB; ++j) acc[j] = zero16();
+
+  // One key tile: S^T and dP^T (lane l holds query l%32), P and dS in fp32, then
+  // dQ^T += K^T dS^T with dS^T as the B operand straight from registers and K^T read from
+  // the row-major K tile by transpose loads.
+  auto compute = [&](int kt, const char* sK, const char* sV) {
+    const int k0 = kt * BC;
+    if (qw >= N || (p.causal && k0 > qw + 31)) return;
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = zero16();
+      dp[kb] = zero16();
+      const int row = kb * 32 + perm_row(l32);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int off = swz_off<CH>(row, 16 * st + 8 * hi);
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sK + off), qf[st], s[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sV + off), gf[st], dp[kb]);
+      }
+    }
+    const bool need_mask = (p.causal && k0 + BC - 1 > qw) || k0 + BC > klim;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(s[kb][i] * sc - lq);
+        if (need_mask) {
+          const int key = k0 + kb * 32 + acc_row(i, hi);
+          const bool ok = key < klim && (!p.causal || key <= myq);
+          if (!ok) pv = 0.f;
+        }
+        dp[kb][i] = pv * (dp[kb][i] - dlq);
+      }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 df = pack8(dp[kb], 8 * half);
+        const int row0 = kb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
+#pragma unroll
+        for (int j = 0; j < DB; ++j) {
+          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
+          const bf16x8 kf = cat_tr(lds_tr4(sK + swz_off<CH>(row0, col)),
+                                   lds_tr4(sK + swz_off<CH>(row0 + 4, col)));
+          acc[j] = mfma32(kf, df, acc[j]);
+        }
+      }
+  };
+
+  // Main loop over pairs of key tiles, one back-edge (see the dK/dV pass).
+  while (kt < nkt) {
+    wait_vm0();
+    __syncthreads();
+    const int kb2 = next_tile(kt + 1);
+    if (kb2 < nkt) issue(kb2, sK1, sV1);
+    compute(kt, sK0, sV0);
+
+    wait_vm0();
+    __syncthreads();
+    const int kc = kb2 < nkt ? next_tile(kb2 + 1) : nkt;
+    if (kc < nkt) issue(kc, sK0, sV0);
+    if (kb2 < nkt) compute(kb2, sK1, sV1);
+    kt = kc;
+  }
+
+  // dQ = scale * dS K (the unmodified K tile was used, so the signed scale applies).
+  if (myq < N) {
+    uint16_t* row = p.dq + hoff + (size_t)myq * D;
+#pragma unroll
+    for (int j = 0; j < DB; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16(acc[j][4 * g + 0] * p.scale, acc[j][4 * g + 1] * p.scale);
+        w[1] = pack_bf16(acc[j][4 * g + 2] * p.scale, acc[j][4 * g + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g + 4 * hi) = w;
+      }
+  }
+}
+
 }  // namespace
 
-hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, float* delta,
-                                 float* dq_accum, int rows, int d, hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
+                                 float* delta, float* lse2, int rows, int d,
+                                 hipStream_t stream) {
   const int rpb = 256 / (d / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
   if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, stream, o, dO, delta,
-                       dq_accum, rows);
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, stream, o, dO, lse, delta,
+                       lse2, rows);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, stream, o, dO, delta, dq_accum,
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, stream, o, dO, lse, delta, lse2,
                        rows);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
-  hipError_t e = launch_bwd_preprocess(p.o, p.dO, p.delta, p.dq_accum, rows, d, stream);
+  hipError_t e = launch_bwd_preprocess(p.o, p.dO, p.lse, p.delta, p.lse2, rows, d, stream);
   if (e != hipSuccess) return e;
-  const int nkt = (p.N + 127) / 128;
-  const dim3 grid((unsigned)nkt * (unsigned)(p.B * p.H));
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_kernel<128>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(bwd_kernel<64>, grid, dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n8 = (long)rows * d / 8;
-  long blocks = (n8 + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     p.dq_accum, p.dq, n8, p.scale);
+  const dim3 grid((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
+  if (d == 128) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), grid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -51,8 +51,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return bf16_bits(a) | (bf16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Eight fp32 accumulator elements [base, base+8) -> one bf16x8 MFMA operand.
@@ -133,6 +137,11 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Two transpose loads (contraction slots 0..3 and 4..7) -> one MFMA operand.
+__device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // LDS transpose load (8 bytes per lane). Within each group of 16 lanes, output lane i
 // receives, as element r (r = 0..3), the (i % 4)-th 16-bit value of the 8 bytes that lane

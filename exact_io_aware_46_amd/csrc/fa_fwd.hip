@@ -40,7 +40,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
   constexpr int LPW = TILE / 1024 / 4;  // 1 KB wave-wide DMA loads per wave per tile
   // Two stages (double buffering) of a K tile and a V tile, both row-major, swizzled.
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];
+  // Each stage is its own array so the compiler can tell the tile being read from the one
+  // being filled and does not wait for the in-flight copy before reading.
+  __shared__ __attribute__((aligned(1024))) char sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILE];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // Asynchronous copy of key tile kt into a stage: every lane moves 16 bytes straight
   // from HBM into LDS. Rows at or past klim fetch row klim-1 instead (they are masked,
   // and reading a valid row keeps every access in bounds).
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](int kt, char* dK, char* dV) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
@@ -93,8 +98,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
       const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
-      g2lds16(K + goff, &smem[stage][0][g * 1024]);
-      g2lds16(V + goff, &smem[stage][1][g * 1024]);
+      g2lds16(K + goff, dK + g * 1024);
+      g2lds16(V + goff, dV + g * 1024);
     }
   };
 
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
 
   int kt = next_tile(0);
-  if (kt < nkt) issue(kt, 0);
+  if (kt < nkt) issue(kt, sK0, sV0);
 
   bf16x8 qf[NS];
 #pragma unroll
@@ -125,19 +130,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = -kInf;
   float l_run = 0.f;
 
-  int stage = 0;
-  while (kt < nkt) {
-    wait_vm0();       // this stage's copies have landed ...
-    __syncthreads();  // ... for every wave, and the other stage is free again
-    const int ktn = next_tile(kt + 1);
-    if (ktn < nkt) issue(ktn, stage ^ 1);
-
+  // One key tile: scores, mask, online softmax, O^T += V^T P^T.
+  auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
-    const char* sK = smem[stage][0];
-    const char* sV = smem[stage][1];
-    kt = ktn;
-    stage ^= 1;
-    if (qw >= N || (p.causal && k0 > qw + 31)) continue;  // nothing allowed for this wave
+    if (qw >= N || (p.causal && k0 > qw + 31)) return;  // nothing allowed for this wave
 
     f32x16 s[KB];
 #pragma unroll
@@ -202,13 +198,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
           const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
-          const i16x4 a0 = lds_tr4(sV + swz_off<CH>(row0, col));
-          const i16x4 a1 = lds_tr4(sV + swz_off<CH>(row0 + 4, col));
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, (i16x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+          const bf16x8 vf = cat_tr(lds_tr4(sV + swz_off<CH>(row0, col)),
+                                   lds_tr4(sV + swz_off<CH>(row0 + 4, col)));
           acc[j] = mfma32(vf, pf, acc[j]);
         }
       }
+  };
+
+  // Main loop, unrolled twice so each half reads one fixed stage while the other fills.
+  while (kt < nkt) {
+    wait_vm0();       // this stage's copies have landed ...
+    __syncthreads();  // ... for every wave, and the other stage is free again
+    int ktn = next_tile(kt + 1);
+    if (ktn < nkt) issue(ktn, sK1, sV1);
+    compute(kt, sK0, sV0);
+    kt = ktn;
+    if (kt >= nkt) break;
+    wait_vm0();
+    __syncthreads();
+    ktn = next_tile(kt + 1);
+    if (ktn < nkt) issue(ktn, sK0, sV0);
+    compute(kt, sK1, sV1);
+    kt = ktn;
   }
 
   const float l_tot = xhalf_sum(l_run);

@@ -80,14 +80,13 @@ int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, 
 int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
                       int d, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: delta (fp32 [B][H][N]) and a fp32 dQ accumulator
- * ([B][H][N][d]). Linear in N. Returns 0 for invalid shapes. */
+/* Bytes of device workspace fa_bwd needs: delta and a log2-scaled copy of LSE (fp32
+ * [B][H][N] each, each padded to 256 bytes). Linear in N. Returns 0 for invalid shapes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward. Inputs: q, k, v, the forward's o and lse, and dO = dL/dO. Outputs dq, dk, dv
  * (bf16). Recomputes P from lse; no N x N matrix is stored. The workspace contents on
- * entry are ignored. dq is accumulated with fp32 atomics, so its low bits may differ from
- * run to run; o, lse, dk and dv do not depend on scheduling. */
+ * entry are ignored. Every output is bitwise reproducible from run to run. */
 int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
            const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv, int B,
            int H, int N, int d, float scale, int causal, const uint8_t* blockmask,

@@ -132,14 +132,13 @@ def test_all_ones_block_mask_is_bitwise_dense(d):
     say(f"[bitexact] ones mask d={d}")
     a = Run(q, k, v, do, 0.125, True)
     b = Run(q, k, v, do, 0.125, True, blockmask=np.ones((3, 3), np.uint8))
-    for name in ("o", "lse", "dk_", "dv_"):
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
         assert _bits_equal(getattr(a, name), getattr(b, name)), name
-    check_grad(to_f64(b.dq_), to_f64(a.dq_), "dQ")
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_padding_poison_is_bitwise_invisible(d):
-    """Keys past kv_len filled with NaN change nothing (O, LSE, dK, dV bitwise)."""
+    """Keys past kv_len filled with NaN change nothing (every output bitwise)."""
     N = 300
     q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=37)
     kv = np.array([211, 64], dtype=np.int32)
@@ -150,9 +149,8 @@ def test_padding_poison_is_bitwise_invisible(d):
     say(f"[bitexact] padding poison d={d}")
     a = Run(q, k, v, do, 0.125, False, kv_len=kv)
     b = Run(q, kp, vp, do, 0.125, False, kv_len=kv)
-    for name in ("o", "lse", "dk_", "dv_"):
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
         assert _bits_equal(getattr(a, name), getattr(b, name)), name
-    assert torch.isfinite(b.dq_.float()).all()
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -189,13 +187,13 @@ def test_causal_future_poison_is_bitwise_invisible(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_forward_and_dkdv_are_deterministic(d):
+def test_all_outputs_are_deterministic(d):
     N = 640
     q, k, v, do = inp.custom_inputs(2, 3, N, d, seed=47)
     say(f"[bitexact] determinism d={d}")
     a = Run(q, k, v, do, 0.125, True)
     b = Run(q, k, v, do, 0.125, True)
-    for name in ("o", "lse", "dk_", "dv_"):
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
         assert _bits_equal(getattr(a, name), getattr(b, name)), name
 
 
