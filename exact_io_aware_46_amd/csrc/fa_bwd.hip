@@ -21,6 +21,8 @@
 // the outer dimension; inner tiles are copied HBM -> LDS by global_load_lds (no
 // registers), double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that
 // must be contraction-major are read with LDS transpose loads.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -65,19 +67,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------- dK, dV pass
 
+// Workgroup = 8 waves = 128 keys of one (b, h). Wave w owns keys 32*(w%4) .. +31 of the
+// tile and, of every 64-query step, the 32 queries of half w/4; the two query halves of a
+// key group sum their dK, dV partials through LDS at the end. Two waves per SIMD let the
+// hardware overlap one wave's exponentials with the other's matrix products. K and V of
+// the tile stay in LDS (row-major, swizzled) for the whole pass.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BKC = 128;           // keys per workgroup (4 waves x 32)
-  constexpr int BQ = 64;             // queries per inner step
-  constexpr int NS = D / 16;         // contraction steps over d
-  constexpr int DB = D / 32;         // 32-wide column blocks over d
-  constexpr int CH = D / 8;          // 16-byte chunks per row of Q, dO
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BKC = 128;            // keys per workgroup
+  constexpr int BQ = 64;              // queries per step
+  constexpr int NS = D / 16;          // contraction steps over d
+  constexpr int DB = D / 32;          // 32-wide column blocks over d
+  constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;
-  constexpr int NQB = BQ / 32;
-  constexpr int QTILE = BQ * ROWB;   // bytes of one Q (or dO) tile
-  constexpr int QLPW = QTILE / 4096; // 1 KB DMA loads per wave per Q tile
+  constexpr int QTILE = BQ * ROWB;    // bytes of one Q (or dO) tile
+  constexpr int KTILE = BKC * ROWB;   // bytes of the K (or V) tile
+  constexpr int QLPW = QTILE / 8192;  // 1 KB DMA loads per wave per Q tile
+  constexpr int KLPW = KTILE / 8192;  // per wave for the K tile
+  static_assert(QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4, "dK/dV reduction space");
   // Every stage is its own array so the compiler can tell the tiles being read from the
   // ones being filled by in-flight copies, and does not wait for those before reading.
+  __shared__ __attribute__((aligned(1024))) char sK[KTILE];
+  __shared__ __attribute__((aligned(1024))) char sV[KTILE];
   __shared__ __attribute__((aligned(1024))) char sQ0[QTILE];
   __shared__ __attribute__((aligned(1024))) char sQ1[QTILE];
   __shared__ __attribute__((aligned(1024))) char sdO0[QTILE];
@@ -94,6 +105,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int kg = wave & 3;   // key group
+  const int qh = wave >> 2;  // query half of each step
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -109,16 +122,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float* __restrict__ DL = p.delta + (size_t)bh * N;
 
   const int k0 = kt * BKC;
-  const int kw = k0 + wave * 32;
+  const int kw = k0 + kg * 32;
   const int mykey = kw + l32;
   int klim = N;
   if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
   const int nb = (N + 127) >> 7;
-
-  // A negative scale is folded into this wave's K registers (used only for S); dK takes
-  // the signed scale at the end.
-  const float sc = fabsf(p.scale) * kLog2e;
-  const uint32_t ksign = p.scale < 0.f ? 0x80008000u : 0u;
+  // Backward needs no running maximum, so the scale (of either sign) goes straight into
+  // the exponent: P = exp2(S * scale * log2(e) - LSE * log2(e)).
+  const float sc = p.scale * kLog2e;
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt_begin = p.causal ? k0 / BQ : 0;
@@ -148,20 +159,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   };
 
   int qt = next_q(qt_begin);
-  if (qt < qt_end) issue_q(qt, sQ0, sdO0, sL0, sD0);
-
-  // This wave's K and V rows as B operands of S = Q K^T and dP = dO V^T (zeros past klim).
-  bf16x8 kreg[NS], vreg[NS];
+  if (qt < qt_end) {
+    // K and V of the tile (rows past klim fetch row klim-1; those keys are masked).
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (mykey < klim) {
-      x = ldg16(K + (size_t)mykey * D + 16 * s + 8 * hi);
-      y = ldg16(V + (size_t)mykey * D + 16 * s + 8 * hi);
+    for (int t = 0; t < KLPW; ++t) {
+      const int g = wave * KLPW + t;
+      const int byte = g * 1024 + lane * 16;
+      const int row = byte / ROWB;
+      const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
+      g2lds16(K + goff, sK + g * 1024);
+      g2lds16(V + goff, sV + g * 1024);
     }
-    x[0] ^= ksign; x[1] ^= ksign; x[2] ^= ksign; x[3] ^= ksign;
-    kreg[s] = as_bf16x8(x);
-    vreg[s] = as_bf16x8(y);
+    issue_q(qt, sQ0, sdO0, sL0, sD0);
   }
 
   f32x16 acc_dk[DB], acc_dv[DB];
@@ -171,66 +181,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     acc_dv[j] = zero16();
   }
 
-  // One query tile against this wave's keys: S and dP (MFMA, [query][key] orientation, so
-  // lane l holds key l%32), P and dS in fp32, then dV += P^T dO and dK += dS^T Q with the
-  // exponentiated tiles as A operands straight from registers and dO^T, Q^T read from the
-  // row-major tiles by transpose loads.
-  auto step = [&](int qt, const char* Qs, const char* dOs, const float* Ls, const float* Ds) {
+  // This wave's 32 queries of a step against its 32 keys: S and dP (MFMA, [query][key]
+  // orientation, so lane l holds key l%32; A from the Q/dO tiles, B from the K/V tile),
+  // P and dS in fp32, then dV += P^T dO and dK += dS^T Q with the exponentiated tiles as
+  // A operands straight from registers and dO^T, Q^T read by transpose loads. Tiles that
+  // need no element mask use an instance without any mask code.
+  const int krow = kg * 32 + l32;
+  auto step = [&](auto masked, int qt, const char* Qs, const char* dOs, const float* Ls,
+                  const float* Ds) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qt * BQ;
-    if ((p.causal && kw > q0 + BQ - 1) || kw >= klim) return;  // nothing allowed here
-    f32x16 s[NQB], dp[NQB];
+    f32x16 s = zero16(), dp = zero16();
+    const int arow = qh * 32 + perm_row(l32);
+#pragma unroll 2
+    for (int k = 0; k < NS; ++k) {
+      const int ao = swz_off<CH>(arow, 16 * k + 8 * hi);
+      const int bo = swz_off<CH>(krow, 16 * k + 8 * hi);
+      s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ao),
+                 *reinterpret_cast<const bf16x8*>(sK + bo), s);
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(dOs + ao),
+                  *reinterpret_cast<const bf16x8*>(sV + bo), dp);
+    }
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      s[qb] = zero16();
-      dp[qb] = zero16();
-      const int row = qb * 32 + perm_row(l32);
+    for (int half = 0; half < 2; ++half) {
+      const int qloc = qh * 32 + 16 * half + 8 * hi;
+      const float4 la = *reinterpret_cast<const float4*>(&Ls[qloc]);
+      const float4 lb = *reinterpret_cast<const float4*>(&Ls[qloc + 4]);
+      const float4 ga = *reinterpret_cast<const float4*>(&Ds[qloc]);
+      const float4 gb = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
+      const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      const float dv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int off = swz_off<CH>(row, 16 * k + 8 * hi);
-        s[qb] = mfma32(*reinterpret_cast<const bf16x8*>(Qs + off), kreg[k], s[qb]);
-        dp[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dOs + off), vreg[k], dp[qb]);
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * half + j;
+        float pv = fast_exp2(s[i] * sc - lv[j]);
+        if constexpr (MASKED) {
+          const int q = q0 + qloc + j;
+          const bool ok = mykey < klim && (!p.causal || mykey <= q) && q < N;
+          pv = ok ? pv : 0.f;
+        }
+        s[i] = pv;
+        dp[i] = pv * (dp[i] - dv[j]);
+      }
+      const bf16x8 pa = pack8(s, 8 * half);
+      const bf16x8 da = pack8(dp, 8 * half);
+      const int row0 = qh * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
+        const int o0 = swz_off<CH>(row0, col), o1 = swz_off<CH>(row0 + 4, col);
+        acc_dv[j] = mfma32(pa, cat_tr(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
+        acc_dk[j] = mfma32(da, cat_tr(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
       }
     }
-    const bool need_mask = (p.causal && kw + 31 > q0) || kw + 32 > klim || q0 + BQ > N;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qloc = qb * 32 + 16 * half + 8 * hi;
-        const float4 la = *reinterpret_cast<const float4*>(&Ls[qloc]);
-        const float4 lb = *reinterpret_cast<const float4*>(&Ls[qloc + 4]);
-        const float4 da = *reinterpret_cast<const float4*>(&Ds[qloc]);
-        const float4 db = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
-        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * half + j;
-          float pv = fast_exp2(s[qb][i] * sc - lv[j]);
-          if (need_mask) {
-            const int q = q0 + qloc + j;
-            const bool ok = mykey < klim && (!p.causal || mykey <= q) && q < N;
-            if (!ok) pv = 0.f;
-          }
-          s[qb][i] = pv;
-          dp[qb][i] = pv * (dp[qb][i] - dv[j]);
-        }
-      }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const bf16x8 pa = pack8(s[qb], 8 * half);
-        const bf16x8 da = pack8(dp[qb], 8 * half);
-        const int row0 = qb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
-#pragma unroll
-        for (int j = 0; j < DB; ++j) {
-          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
-          const int o0 = swz_off<CH>(row0, col), o1 = swz_off<CH>(row0 + 4, col);
-          acc_dv[j] = mfma32(pa, cat_tr(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
-          acc_dk[j] = mfma32(da, cat_tr(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
-        }
-      }
+  };
+  auto run_step = [&](int qt, const char* Qs, const char* dOs, const float* Ls,
+                      const float* Ds) {
+    const int qw0 = qt * BQ + qh * 32;  // this wave's first query
+    if ((p.causal && kw > qw0 + 31) || kw >= klim || qw0 >= N) return;
+    if ((p.causal && kw + 31 > qw0) || kw + 32 > klim || qw0 + 32 > N)
+      step(std::true_type{}, qt, Qs, dOs, Ls, Ds);
+    else
+      step(std::false_type{}, qt, Qs, dOs, Ls, Ds);
   };
 
   // Main loop over pairs of query tiles (stage 0, then stage 1), one back-edge, so each
@@ -240,28 +252,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();  // stage 0 has landed everywhere; stage 1 is free
     const int qb = next_q(qt + 1);
     if (qb < qt_end) issue_q(qb, sQ1, sdO1, sL1, sD1);
-    step(qt, sQ0, sdO0, sL0, sD0);
+    run_step(qt, sQ0, sdO0, sL0, sD0);
 
     wait_vm0();
     __syncthreads();  // stage 1 has landed; stage 0 is free
     const int qc = qb < qt_end ? next_q(qb + 1) : qt_end;
     if (qc < qt_end) issue_q(qc, sQ0, sdO0, sL0, sD0);
-    if (qb < qt_end) step(qb, sQ1, sdO1, sL1, sD1);
+    if (qb < qt_end) run_step(qb, sQ1, sdO1, sL1, sD1);
     qt = qc;
   }
 
-  // Epilogue: dK = scale * acc_dk (K's sign was only folded into S), dV = acc_dv.
+  // The two query halves of each key group add their partial dK, dV through LDS (the
+  // tiles are no longer needed): half 1 writes fp32 partials, half 0 adds and stores.
+  __syncthreads();
+  char* bufk = kg < 2 ? sK + kg * (KTILE / 2) : sV + (kg - 2) * (KTILE / 2);
+  char* bufv = kg == 0 ? sQ0 : kg == 1 ? sQ1 : kg == 2 ? sdO0 : sdO1;
+  auto slot = [&](int j, int i) {
+    return ((8 * (i >> 2) + 4 * hi + (i & 3)) * D + 32 * j + l32) * 4;
+  };
+  if (qh == 1) {
 #pragma unroll
-  for (int j = 0; j < DB; ++j)
+    for (int j = 0; j < DB; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (key < N) {
-        const size_t off = hoff + (size_t)key * D + j * 32 + l32;
-        p.dk[off] = (uint16_t)bf16_bits(acc_dk[j][i] * p.scale);
-        p.dv[off] = (uint16_t)bf16_bits(acc_dv[j][i]);
+      for (int i = 0; i < 16; ++i) {
+        *reinterpret_cast<float*>(bufk + slot(j, i)) = acc_dk[j][i];
+        *reinterpret_cast<float*>(bufv + slot(j, i)) = acc_dv[j][i];
       }
-    }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    // dK = scale * (dS^T Q), dV = P^T dO.
+#pragma unroll
+    for (int j = 0; j < DB; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
+        const float dk = acc_dk[j][i] + *reinterpret_cast<const float*>(bufk + slot(j, i));
+        const float dv = acc_dv[j][i] + *reinterpret_cast<const float*>(bufv + slot(j, i));
+        if (key < N) {
+          const size_t off = hoff + (size_t)key * D + j * 32 + l32;
+          p.dk[off] = (uint16_t)bf16_bits(dk * p.scale);
+          p.dv[off] = (uint16_t)bf16_bits(dv);
+        }
+      }
+  }
 }
 
 // ----------------------------------------------------------------- dQ pass
@@ -333,14 +367,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  const float sc = fabsf(p.scale) * kLog2e;
-  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+  // No running maximum here, so the scale (of either sign) goes straight into the
+  // exponent: P = exp2(S * scale * log2(e) - LSE * log2(e)).
+  const float sc = p.scale * kLog2e;
 
   int kt = next_tile(0);
   if (kt < nkt) issue(kt, sK0, sV0);
 
-  // This lane's query row of Q (sign-adjusted) and dO, as B operands of S^T = K Q^T and
-  // dP^T = V dO^T; its log2-scaled LSE and D.
+  // This lane's query row of Q and dO, as B operands of S^T = K Q^T and dP^T = V dO^T;
+  // its log2-scaled LSE and D.
   bf16x8 qf[NS], gf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -349,7 +384,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
       y = ldg16(dO + (size_t)myq * D + 16 * s + 8 * hi);
     }
-    x[0] ^= qsign; x[1] ^= qsign; x[2] ^= qsign; x[3] ^= qsign;
     qf[s] = as_bf16x8(x);
     gf[s] = as_bf16x8(y);
   }
@@ -424,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     kt = kc;
   }
 
-  // dQ = scale * dS K (the unmodified K tile was used, so the signed scale applies).
+  // dQ = scale * dS K.
   if (myq < N) {
     uint16_t* row = p.dq + hoff + (size_t)myq * D;
 #pragma unroll
@@ -461,11 +495,11 @@ hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
   if (d == 128) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), grid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), grid, dim3(256), 0, stream, p);
   }
