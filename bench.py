@@ -272,7 +272,7 @@ def main():
                          "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(wl.name, "fwd_kernel",
-                                                     [f"fwd_kernel<{wl.d}, {64 if wl.d == 128 else 128}>"])},
+                                                     [f"fwd_kernel<{wl.d}, 64>"])},
     }
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf

@@ -301,15 +301,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 // ----------------------------------------------------------------- dQ pass
 
 template <int D, int BC>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  constexpr int BR = 128;           // queries per workgroup
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;
   constexpr int KB = BC / 32;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
-  constexpr int LPW = TILE / 4096;
+  constexpr int LPW = TILE / 8192;  // 1 KB DMA loads per wave per tile
   __shared__ __attribute__((aligned(1024))) char sK0[TILE];
   __shared__ __attribute__((aligned(1024))) char sV0[TILE];
   __shared__ __attribute__((aligned(1024))) char sK1[TILE];
@@ -345,11 +345,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   if (p.causal) kend = min(kend, q0 + BR);
   const int nkt = (kend + BC - 1) / BC;
   const int nb = (N + 127) >> 7;
-  const uint8_t* bmrow = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+  // Block table rows of the workgroup's two 128-query blocks and of this wave's block.
+  const uint8_t* bm0 = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+  const uint8_t* bm1 = (bm0 && (q0 >> 7) + 1 < nb) ? bm0 + nb : bm0;
+  const uint8_t* bmw = (wave < 4) ? bm0 : bm1;
 
+  // Next key tile at or after kt that either query block keeps (all without a table).
   auto next_tile = [&](int kt) {
-    if (bmrow)
-      while (kt < nkt && !bmrow[(kt * BC) >> 7]) ++kt;
+    if (bm0)
+      while (kt < nkt && !bm0[(kt * BC) >> 7] && !bm1[(kt * BC) >> 7]) ++kt;
     return kt;
   };
   // Key tile kt -> stage (K and V rows; rows at or past klim fetch row klim-1, masked).
@@ -400,6 +404,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || (p.causal && k0 > qw + 31)) return;
+    if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
     f32x16 s[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -493,15 +498,16 @@ hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
   hipError_t e = launch_bwd_preprocess(p.o, p.dO, p.lse, p.delta, p.lse2, rows, d, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
+  const unsigned bh = (unsigned)(p.B * p.H);
+  const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);
   if (d == 128) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), g_q, dim3(512), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), g_q, dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -13,7 +13,8 @@
 // them).
 //
 // gfx950 mapping:
-//   workgroup = 4 waves = 128 queries of one (b, h); wave w owns queries 32w .. 32w+31.
+//   workgroup = 8 waves = 256 queries of one (b, h); wave w owns queries 32w .. 32w+31
+//   (two waves per SIMD, and every K/V tile copied into LDS serves 256 queries).
 //   Key tiles (BC keys) of K and V are copied HBM -> LDS by the DMA path of the vector
 //   memory unit (global_load_lds, no registers), double-buffered so the next tile streams
 //   in while the current one is used, and kept row-major with XOR-swizzled 16-byte chunks.
@@ -30,15 +31,15 @@ namespace fa {
 namespace {
 
 template <int D, int BC>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  constexpr int BR = 128;           // queries per workgroup
+__global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
+  constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;        // contraction steps of the score MFMA
   constexpr int KB = BC / 32;       // 32-key blocks per key tile
   constexpr int DB = D / 32;        // 32-wide column blocks of O
   constexpr int CH = D / 8;         // 16-byte chunks per row
   constexpr int ROWB = D * 2;       // bytes per row
   constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
-  constexpr int LPW = TILE / 1024 / 4;  // 1 KB wave-wide DMA loads per wave per tile
+  constexpr int LPW = TILE / 1024 / 8;  // 1 KB wave-wide DMA loads per wave per tile
   // Two stages (double buffering) of a K tile and a V tile, both row-major, swizzled.
   // Each stage is its own array so the compiler can tell the tile being read from the one
   // being filled and does not wait for the in-flight copy before reading.
@@ -78,12 +79,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (p.causal) kend = min(kend, q0 + BR);
   const int nkt = (kend + BC - 1) / BC;
   const int nb = (N + 127) >> 7;
-  const uint8_t* bmrow = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+  // Block table rows of the workgroup's two 128-query blocks (the second may not exist)
+  // and of this wave's block.
+  const uint8_t* bm0 = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
+  const uint8_t* bm1 = (bm0 && (q0 >> 7) + 1 < nb) ? bm0 + nb : bm0;
+  const uint8_t* bmw = (wave < 4) ? bm0 : bm1;
 
-  // Next key tile at or after kt that the block table keeps (all of them without one).
+  // Next key tile at or after kt that either query block keeps (all without a table).
   auto next_tile = [&](int kt) {
-    if (bmrow)
-      while (kt < nkt && !bmrow[(kt * BC) >> 7]) ++kt;
+    if (bm0)
+      while (kt < nkt && !bm0[(kt * BC) >> 7] && !bm1[(kt * BC) >> 7]) ++kt;
     return kt;
   };
   // Asynchronous copy of key tile kt into a stage: every lane moves 16 bytes straight
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || (p.causal && k0 > qw + 31)) return;  // nothing allowed for this wave
+    if (bmw && !bmw[k0 >> 7]) return;                   // block masked for this wave
 
     f32x16 s[KB];
 #pragma unroll
@@ -243,12 +249,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream) {
-  const int nqt = (p.N + 127) / 128;
+  const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<128, 64>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<128, 64>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<64, 128>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<64, 128>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
