@@ -405,37 +405,31 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     const int k0 = kt * BC;
     if (qw >= N || (p.causal && k0 > qw + 31)) return;
     if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
-    f32x16 s[KB], dp[KB];
+    const bool need_mask = (p.causal && k0 + BC - 1 > qw) || k0 + BC > klim;
+    // One 32-key block at a time, so only one block of S and dP is live.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = zero16();
-      dp[kb] = zero16();
+      f32x16 s = zero16(), dp = zero16();
       const int row = kb * 32 + perm_row(l32);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const int off = swz_off<CH>(row, 16 * st + 8 * hi);
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sK + off), qf[st], s[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sV + off), gf[st], dp[kb]);
+        s = mfma32(*reinterpret_cast<const bf16x8*>(sK + off), qf[st], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(sV + off), gf[st], dp);
       }
-    }
-    const bool need_mask = (p.causal && k0 + BC - 1 > qw) || k0 + BC > klim;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(s[kb][i] * sc - lq);
+        float pv = fast_exp2(s[i] * sc - lq);
         if (need_mask) {
           const int key = k0 + kb * 32 + acc_row(i, hi);
           const bool ok = key < klim && (!p.causal || key <= myq);
           if (!ok) pv = 0.f;
         }
-        dp[kb][i] = pv * (dp[kb][i] - dlq);
+        dp[i] = pv * (dp[i] - dlq);
       }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const bf16x8 df = pack8(dp[kb], 8 * half);
+        const bf16x8 df = pack8(dp, 8 * half);
         const int row0 = kb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
@@ -445,6 +439,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           acc[j] = mfma32(kf, df, acc[j]);
         }
       }
+    }
   };
 
   // Main loop over pairs of key tiles, one back-edge (see the dK/dV pass).

@@ -108,13 +108,20 @@ __device__ __forceinline__ int tchunk(int row, int chunk) { return chunk ^ ((row
 // Row-major tiles in LDS with 16-byte chunks XOR-swizzled by row.
 //
 // A tile row holds CH 16-byte chunks (CH = d / 8). Logical chunk c of row k is stored at
-// physical chunk c ^ swz<CH>(k). The swizzle is a permutation of the low row bits chosen
-// so that (a) the 16 rows read by one 16-lane phase of a row-major MFMA operand load hit
-// 16 different bank groups, and (b) the rows read by one LDS transpose load spread too.
+// physical chunk c ^ swz<CH>(k). With 64 four-byte banks (256 bytes):
+//  (a) a row-major MFMA operand load (16 lanes per cycle, 16 rows, one chunk each) needs
+//      swz to be one-to-one on the rows that share a bank window (16 rows for d = 128,
+//      the 8 rows of one parity for d = 64);
+//  (b) a transpose load (32 lanes per cycle: 4 consecutive rows, 4 consecutive chunks
+//      4j .. 4j+3 each, 8 bytes per lane) needs the rows that share a bank window to move
+//      the chunk group to different places, i.e. bits 2-3 (d = 128) or bit 2 (d = 64) of
+//      swz must differ between them.
+// d = 128: swap the two bit pairs of the low row nibble. d = 64: bit 2 from row bit 1,
+// bits 0-1 from row bits 2-3.
 template <int CH>
 __device__ __forceinline__ int swz(int k) {
-  if constexpr (CH == 16) return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8);
-  else return (((k >> 1) & 3) << 1) | ((k >> 3) & 1);
+  if constexpr (CH == 16) return ((k & 3) << 2) | ((k >> 2) & 3);
+  else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
 }
 
 // Byte offset of element `col` (a multiple of 4) of row `row` in a swizzled tile.
