@@ -87,12 +87,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   static_assert(QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4, "dK/dV reduction space");
   // Every stage is its own array so the compiler can tell the tiles being read from the
   // ones being filled by in-flight copies, and does not wait for those before reading.
-  __shared__ __attribute__((aligned(1024))) char sK[KTILE];
-  __shared__ __attribute__((aligned(1024))) char sV[KTILE];
+  // The per-step stages come first so that their offsets fit the 16-bit immediate of
+  // the LDS instructions.
   __shared__ __attribute__((aligned(1024))) char sQ0[QTILE];
   __shared__ __attribute__((aligned(1024))) char sQ1[QTILE];
   __shared__ __attribute__((aligned(1024))) char sdO0[QTILE];
   __shared__ __attribute__((aligned(1024))) char sdO1[QTILE];
+  __shared__ __attribute__((aligned(1024))) char sK[KTILE];
+  __shared__ __attribute__((aligned(1024))) char sV[KTILE];
   __shared__ __attribute__((aligned(256))) float sL0[BQ];
   __shared__ __attribute__((aligned(256))) float sL1[BQ];
   __shared__ __attribute__((aligned(256))) float sD0[BQ];
@@ -186,21 +188,29 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   // P and dS in fp32, then dV += P^T dO and dK += dS^T Q with the exponentiated tiles as
   // A operands straight from registers and dO^T, Q^T read by transpose loads. Tiles that
   // need no element mask use an instance without any mask code.
+  // Lane offsets of the operand loads. Within a row, the swizzled offset of contraction
+  // step k is the offset of step 0 XOR (k << 5), and that of column block j of a transpose
+  // load is the offset of block 0 XOR (j << 6); sixteen rows further is +16 rows.
   const int krow = kg * 32 + l32;
+  const int a_off = swz_off<CH>(qh * 32 + perm_row(l32), 8 * hi);  // Q, dO rows (A operand)
+  const int b_off = swz_off<CH>(krow, 8 * hi);                       // K, V rows (B operand)
+  const int t_row = qh * 32 + 8 * (grp >> 1) + (t16 >> 2);
+  const int t_col = 16 * (grp & 1) + 4 * (t16 & 3);
+  const int t_off0 = swz_off<CH>(t_row, t_col), t_off1 = swz_off<CH>(t_row + 4, t_col);
   auto step = [&](auto masked, int qt, const char* Qs, const char* dOs, const float* Ls,
                   const float* Ds) {
     constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qt * BQ;
     f32x16 s = zero16(), dp = zero16();
-    const int arow = qh * 32 + perm_row(l32);
-#pragma unroll 2
+#pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int ao = swz_off<CH>(arow, 16 * k + 8 * hi);
-      const int bo = swz_off<CH>(krow, 16 * k + 8 * hi);
+      const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
       s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ao),
                  *reinterpret_cast<const bf16x8*>(sK + bo), s);
       dp = mfma32(*reinterpret_cast<const bf16x8*>(dOs + ao),
                   *reinterpret_cast<const bf16x8*>(sV + bo), dp);
+      // Keep the scheduler from hoisting every operand load of the loop to its top.
+      if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -225,11 +235,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       }
       const bf16x8 pa = pack8(s, 8 * half);
       const bf16x8 da = pack8(dp, 8 * half);
-      const int row0 = qh * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
+      const int hoffb = half * 16 * ROWB;
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
-        const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
-        const int o0 = swz_off<CH>(row0, col), o1 = swz_off<CH>(row0 + 4, col);
+        const int o0 = hoffb + (t_off0 ^ (j << 6)), o1 = hoffb + (t_off1 ^ (j << 6));
         acc_dv[j] = mfma32(pa, cat_tr(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
         acc_dk[j] = mfma32(da, cat_tr(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
       }
