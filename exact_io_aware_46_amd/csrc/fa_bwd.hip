@@ -407,6 +407,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int j = 0; j < DB; ++j) acc[j] = zero16();
 
+  // Lane offsets of the operand loads (see the dK/dV pass): K and V rows as the A operand
+  // (step st: XOR (st << 5)), and the K^T transpose loads (column block j: XOR (j << 6)).
+  const int a_off = swz_off<CH>(perm_row(l32), 8 * hi);
+  const int t_row = 8 * (grp >> 1) + (t16 >> 2);
+  const int t_col = 16 * (grp & 1) + 4 * (t16 & 3);
+  const int t_off0 = swz_off<CH>(t_row, t_col), t_off1 = swz_off<CH>(t_row + 4, t_col);
+
   // One key tile: S^T and dP^T (lane l holds query l%32), P and dS in fp32, then
   // dQ^T += K^T dS^T with dS^T as the B operand straight from registers and K^T read from
   // the row-major K tile by transpose loads.
@@ -419,12 +426,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s = zero16(), dp = zero16();
-      const int row = kb * 32 + perm_row(l32);
+      const int kbo = kb * 32 * ROWB;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const int off = swz_off<CH>(row, 16 * st + 8 * hi);
+        const int off = kbo + (a_off ^ (st << 5));
         s = mfma32(*reinterpret_cast<const bf16x8*>(sK + off), qf[st], s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(sV + off), gf[st], dp);
+        if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -439,12 +447,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const bf16x8 df = pack8(dp, 8 * half);
-        const int row0 = kb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
+        const int ho = kbo + half * 16 * ROWB;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
-          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
-          const bf16x8 kf = cat_tr(lds_tr4(sK + swz_off<CH>(row0, col)),
-                                   lds_tr4(sK + swz_off<CH>(row0 + 4, col)));
+          const int o0 = ho + (t_off0 ^ (j << 6)), o1 = ho + (t_off1 ^ (j << 6));
+          const bf16x8 kf = cat_tr(lds_tr4(sK + o0), lds_tr4(sK + o1));
           acc[j] = mfma32(kf, df, acc[j]);
         }
       }

@@ -135,6 +135,14 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   float m_run = -kInf;
   float l_run = 0.f;
 
+  // Lane offsets of the LDS operand loads. Within a swizzled row the offset of contraction
+  // step st is that of step 0 XOR (st << 5); for a transpose load, column block j is
+  // block 0 XOR (j << 6); 16 or 32 rows further is additive.
+  const int k_off = swz_off<CH>(perm_row(l32), 8 * hi);
+  const int t_row = 8 * (grp >> 1) + (t16 >> 2);
+  const int t_col = 16 * (grp & 1) + 4 * (t16 & 3);
+  const int t_off0 = swz_off<CH>(t_row, t_col), t_off1 = swz_off<CH>(t_row + 4, t_col);
+
   // One key tile: scores, mask, online softmax, O^T += V^T P^T.
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
@@ -145,11 +153,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
-      const int row = kb * 32 + perm_row(l32);
 #pragma unroll
       for (int st = 0; st < NS; ++st)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sK + swz_off<CH>(row, 16 * st + 8 * hi)),
-                       qf[st], s[kb]);
+        s[kb] = mfma32(
+            *reinterpret_cast<const bf16x8*>(sK + kb * 32 * ROWB + (k_off ^ (st << 5))), qf[st],
+            s[kb]);
     }
 
     if ((p.causal && k0 + BC - 1 > qw) || k0 + BC > klim) {
@@ -200,12 +208,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const bf16x8 pf = pack8(s[kb], 8 * half);
-        const int row0 = kb * 32 + 16 * half + 8 * (grp >> 1) + (t16 >> 2);
+        const int ho = (kb * 32 + 16 * half) * ROWB;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
-          const int col = 32 * j + 16 * (grp & 1) + 4 * (t16 & 3);
-          const bf16x8 vf = cat_tr(lds_tr4(sV + swz_off<CH>(row0, col)),
-                                   lds_tr4(sV + swz_off<CH>(row0 + 4, col)));
+          const bf16x8 vf = cat_tr(lds_tr4(sV + ho + (t_off0 ^ (j << 6))),
+                                   lds_tr4(sV + ho + (t_off1 ^ (j << 6))));
           acc[j] = mfma32(vf, pf, acc[j]);
         }
       }
