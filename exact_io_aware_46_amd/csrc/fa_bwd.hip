@@ -87,12 +87,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   static_assert(QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4, "dK/dV reduction space");
   // Every stage is its own array so the compiler can tell the tiles being read from the
   // ones being filled by in-flight copies, and does not wait for those before reading.
-  // The per-step stages come first so that their offsets fit the 16-bit immediate of
-  // the LDS instructions.
-  __shared__ __attribute__((aligned(1024))) char sQ0[QTILE];
-  __shared__ __attribute__((aligned(1024))) char sQ1[QTILE];
-  __shared__ __attribute__((aligned(1024))) char sdO0[QTILE];
-  __shared__ __attribute__((aligned(1024))) char sdO1[QTILE];
+  // The per-step stages carry the larger alignment, which places them at the lowest LDS
+  // addresses, so their offsets fit the 16-bit immediate of the LDS instructions.
+  __shared__ __attribute__((aligned(4096))) char sQ0[QTILE];
+  __shared__ __attribute__((aligned(4096))) char sQ1[QTILE];
+  __shared__ __attribute__((aligned(4096))) char sdO0[QTILE];
+  __shared__ __attribute__((aligned(4096))) char sdO1[QTILE];
   __shared__ __attribute__((aligned(1024))) char sK[KTILE];
   __shared__ __attribute__((aligned(1024))) char sV[KTILE];
   __shared__ __attribute__((aligned(256))) float sL0[BQ];
