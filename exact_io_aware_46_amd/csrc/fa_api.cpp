@@ -104,7 +104,7 @@ int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, 
   const size_t tbytes = (size_t)B * H * N * d * 2;
   const Range rd = span(delta, (size_t)B * H * N * 4);
   if (overlap(rd, span(o, tbytes)) || overlap(rd, span(dO, tbytes))) return FA_ERR_ALIAS;
-  if (fa::launch_bwd_preprocess(o, dO, nullptr, delta, nullptr, B * H * N, d,
+  if (fa::launch_bwd_preprocess(o, dO, nullptr, delta, nullptr, B * H * N, d, 1.f,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
@@ -147,7 +147,7 @@ int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf1
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.blockmask = blockmask;
   p.kv_len = kv_len;
-  p.delta = reinterpret_cast<float*>(ws);
+  p.ndelta = reinterpret_cast<float*>(ws);
   p.lse2 = reinterpret_cast<float*>(ws + round_up(rows * 4, kWsAlign));
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;

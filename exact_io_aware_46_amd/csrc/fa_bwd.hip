@@ -31,14 +31,17 @@ namespace {
 
 // ---------------------------------------------------------------- preprocess
 
-// Per row: delta = sum_c dO*O (fp32); optionally lse2 = LSE*log2(e) with a fully masked
-// row (LSE = -inf) mapped to +inf, so exp2(s - lse2) = 0 needs no test in the main passes.
+// Per row: delta = dsign * sum_c dO*O (fp32); optionally lse2 = LSE*log2(e) with a fully
+// masked row (LSE = -inf) mapped to +inf, so exp2(s - lse2) = 0 needs no test in the main
+// passes. The main passes take D negated (dsign = -1): the dK/dV pass then starts the dP
+// accumulator at -D and gets dP - D from the matrix unit.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int rows) {
+                                                      float* __restrict__ lse2, int rows,
+                                                      float dsign) {
   constexpr int TPR = D / 8;        // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;    // rows per block
   const int tid = threadIdx.x;
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
   if (row < rows && c == 0) {
-    delta[row] = acc;
+    delta[row] = dsign * acc;
     if (lse2) {
       const float l = lse[row];
       lse2[row] = l == -kInf ? kInf : l * kLog2e;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const uint16_t* __restrict__ V = p.v + hoff;
   const uint16_t* __restrict__ dO = p.dO + hoff;
   const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
-  const float* __restrict__ DL = p.delta + (size_t)bh * N;
+  const float* __restrict__ DL = p.ndelta + (size_t)bh * N;
 
   const int k0 = kt * BKC;
   const int kw = k0 + kg * 32;
@@ -201,7 +204,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
                   const float* Ds) {
     constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qt * BQ;
-    f32x16 s = zero16(), dp = zero16();
+    // dP starts at -D of each query row (accumulator element i of lane half hi belongs to
+    // query 16*(i/8) + 8*hi + i%8 of this wave's 32), so the products add dO V^T to it.
+    f32x16 s = zero16(), dp;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int qloc = qh * 32 + 16 * half + 8 * hi;
+      const float4 ga = *reinterpret_cast<const float4*>(&Ds[qloc]);
+      const float4 gb = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
+      dp[8 * half + 0] = ga.x; dp[8 * half + 1] = ga.y; dp[8 * half + 2] = ga.z;
+      dp[8 * half + 3] = ga.w; dp[8 * half + 4] = gb.x; dp[8 * half + 5] = gb.y;
+      dp[8 * half + 6] = gb.z; dp[8 * half + 7] = gb.w;
+    }
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
@@ -217,10 +231,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       const int qloc = qh * 32 + 16 * half + 8 * hi;
       const float4 la = *reinterpret_cast<const float4*>(&Ls[qloc]);
       const float4 lb = *reinterpret_cast<const float4*>(&Ls[qloc + 4]);
-      const float4 ga = *reinterpret_cast<const float4*>(&Ds[qloc]);
-      const float4 gb = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
       const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-      const float dv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * half + j;
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
           pv = ok ? pv : 0.f;
         }
         s[i] = pv;
-        dp[i] = pv * (dp[i] - dv[j]);
+        dp[i] = pv * dp[i];  // dS = P (dP - D)
       }
       const bf16x8 pa = pack8(s, 8 * half);
       const bf16x8 da = pack8(dp, 8 * half);
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     gf[s] = as_bf16x8(y);
   }
   const float lq = myq < N ? p.lse2[(size_t)bh * N + myq] : kInf;  // +inf: P = 0
-  const float dlq = myq < N ? p.delta[(size_t)bh * N + myq] : 0.f;
+  const float ndq = myq < N ? p.ndelta[(size_t)bh * N + myq] : 0.f;  // -D
 
   f32x16 acc[DB];
 #pragma unroll
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           const bool ok = key < klim && (!p.causal || key <= myq);
           if (!ok) pv = 0.f;
         }
-        dp[i] = pv * (dp[i] - dlq);
+        dp[i] = pv * (dp[i] + ndq);
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -492,22 +503,23 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
-                                 float* delta, float* lse2, int rows, int d,
+                                 float* delta, float* lse2, int rows, int d, float dsign,
                                  hipStream_t stream) {
   const int rpb = 256 / (d / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
   if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows);
+                       lse2, rows, dsign);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, stream, o, dO, lse, delta, lse2,
-                       rows);
+                       rows, dsign);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
-  hipError_t e = launch_bwd_preprocess(p.o, p.dO, p.lse, p.delta, p.lse2, rows, d, stream);
+  hipError_t e =
+      launch_bwd_preprocess(p.o, p.dO, p.lse, p.ndelta, p.lse2, rows, d, -1.f, stream);
   if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);

@@ -31,7 +31,7 @@ struct BwdParams {
   uint16_t* dv;
   const uint8_t* blockmask;
   const int32_t* kv_len;
-  float* delta;     // [B][H][N]: rowsum(dO * O)
+  float* ndelta;    // [B][H][N]: -rowsum(dO * O)
   float* lse2;      // [B][H][N]: LSE * log2(e), +inf for a fully masked row
   int B, H, N;
   float scale;
@@ -40,8 +40,9 @@ struct BwdParams {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
+// delta = dsign * rowsum(dO * O); lse2 = LSE * log2(e) when lse2 is not null.
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
-                                 float* delta, float* lse2, int rows, int d,
+                                 float* delta, float* lse2, int rows, int d, float dsign,
                                  hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 
