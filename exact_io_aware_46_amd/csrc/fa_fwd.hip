@@ -261,7 +261,7 @@ hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream) {
   if (d == 128)
     hipLaunchKernelGGL((fwd_kernel<128, 64>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<64, 128>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<64, 64>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
