@@ -30,7 +30,12 @@ notes of the repository):
 * scale multiplies Q K^T before masking; the float32 scale is widened exactly;
 * causal means key j is allowed for query i iff j <= i (equal lengths);
 * key padding (valid length L_b per batch entry) masks keys j >= L_b for every query;
-* the three masks compose by logical AND;
+* sliding-window (local) attention, which the deployment page lists as a supported option
+  ("IO感知计算如何重塑Transformer内存优化技术格局", bxzpzcl.cn, section 高级功能配置) without
+  defining it, is read as a window (left, right) on the key index relative to the query:
+  key j is allowed for query i iff i - left <= j <= i + right, a negative bound meaning
+  no limit on that side (so (-1, 0) is the causal mask);
+* the masks compose by logical AND;
 * a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
 * backward is the derivative of the scalar L = sum(dO * O) with respect to Q, K, V:
   dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic, dS = P * (dP - D),
@@ -64,14 +69,22 @@ def as_f64(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float64)
 
 
-def allowed(rows: np.ndarray, n_keys: int, causal: bool, blockmask, kv_len_b) -> np.ndarray:
-    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend to key j."""
+def allowed(rows: np.ndarray, n_keys: int, causal: bool, blockmask, kv_len_b,
+            window=None) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where query ``rows[r]`` may attend to key j.
+    ``window`` is None or (left, right): keys i-left .. i+right, a negative bound = none."""
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(n_keys, dtype=np.int64)[None, :]
     i = rows[:, None]
     ok = np.ones((rows.size, n_keys), dtype=bool)
     if causal:
         ok &= j <= i
+    if window is not None:
+        left, right = int(window[0]), int(window[1])
+        if left >= 0:
+            ok &= j >= i - left
+        if right >= 0:
+            ok &= j <= i + right
     if blockmask is not None:
         bm = np.asarray(blockmask) != 0
         ok &= bm[i // MASK_BLOCK, j // MASK_BLOCK]
@@ -116,7 +129,7 @@ def _head_view(x, b, h):
 
 
 def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
-                 rows=None, panel=DEFAULT_PANEL):
+                 rows=None, panel=DEFAULT_PANEL, window=None):
     """One head: returns (O[rows], LSE[rows]) in float64."""
     N = Kh.shape[0]
     s = _scale64(scale)
@@ -125,7 +138,7 @@ def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
     LSE = np.zeros(rows.size)
     for r0 in range(0, rows.size, panel):
         rr = rows[r0:r0 + panel]
-        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b))
+        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b, window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
         O[r0:r0 + rr.size] = P @ Vh
@@ -134,7 +147,7 @@ def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
 
 
 def head_backward(Qh, Kh, Vh, dOh, scale, causal=False, blockmask=None, kv_len_b=None,
-                  panel=DEFAULT_PANEL):
+                  panel=DEFAULT_PANEL, window=None):
     """One head, all rows: returns dict with O, LSE, D, dQ, dK, dV (float64)."""
     N, d = Kh.shape
     s = _scale64(scale)
@@ -143,7 +156,7 @@ def head_backward(Qh, Kh, Vh, dOh, scale, causal=False, blockmask=None, kv_len_b
     out["D"] = np.zeros(N)
     for r0 in range(0, N, panel):
         rr = np.arange(r0, min(N, r0 + panel))
-        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b))
+        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b, window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
         O = P @ Vh
@@ -164,7 +177,7 @@ def _kv_len_b(kv_len, b):
     return None if kv_len is None else int(np.asarray(kv_len)[b])
 
 
-def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None):
+def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None):
     """All heads. q, k, v: [B][H][N][d] (bf16 bits or reals). Returns O, LSE (float64)."""
     B, H, N, d = q.shape
     O = np.zeros((B, H, N, d))
@@ -173,11 +186,11 @@ def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None):
         for h in range(H):
             O[b, h], LSE[b, h] = head_forward(_head_view(q, b, h), _head_view(k, b, h),
                                               _head_view(v, b, h), scale, causal, blockmask,
-                                              _kv_len_b(kv_len, b))
+                                              _kv_len_b(kv_len, b), window=window)
     return O, LSE
 
 
-def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None):
+def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None, window=None):
     """All heads. Returns dict of float64 arrays: O, LSE, D, dQ, dK, dV."""
     B, H, N, d = q.shape
     res = {key: np.zeros((B, H, N, d)) for key in ("O", "dQ", "dK", "dV")}
@@ -187,25 +200,28 @@ def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None):
         for h in range(H):
             r = head_backward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
                               _head_view(do, b, h), scale, causal, blockmask,
-                              _kv_len_b(kv_len, b))
+                              _kv_len_b(kv_len, b), window=window)
             for key in res:
                 res[key][b, h] = r[key]
     return res
 
 
-def forward_rows(q, k, v, scale, sel, causal=False, blockmask=None, kv_len=None):
+def forward_rows(q, k, v, scale, sel, causal=False, blockmask=None, kv_len=None,
+                 window=None):
     """Sampled rows: ``sel`` is a sequence of (b, h, i). Returns O [len, d], LSE [len]."""
     d = q.shape[3]
     O = np.zeros((len(sel), d))
     LSE = np.zeros(len(sel))
     for n, (b, h, i) in enumerate(sel):
         o, l = head_forward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
-                            scale, causal, blockmask, _kv_len_b(kv_len, b), rows=[i])
+                            scale, causal, blockmask, _kv_len_b(kv_len, b), rows=[i],
+                            window=window)
         O[n], LSE[n] = o[0], l[0]
     return O, LSE
 
 
-def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None):
+def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None,
+            window=None):
     """Sampled dQ rows (each row of dQ depends only on its own row of P and dP)."""
     N, d = q.shape[2], q.shape[3]
     s = _scale64(scale)
@@ -213,7 +229,8 @@ def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None):
     for n, (b, h, i) in enumerate(sel):
         Qh, Kh, Vh = _head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h)
         dOi = as_f64(do[b, h, i])[None, :]
-        S = _scores(Qh[[i]], Kh, s, allowed([i], N, causal, blockmask, _kv_len_b(kv_len, b)))
+        S = _scores(Qh[[i]], Kh, s,
+                    allowed([i], N, causal, blockmask, _kv_len_b(kv_len, b), window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
         O = P @ Vh

@@ -398,3 +398,129 @@ def test_planted_forward_mistakes_are_caught():
     # the real oracle passes it
     O, _ = orc.head_forward(q, k, v, 0.125, causal=True)
     assert np.abs(O - expect).max() < 1e-12
+
+
+# ------------------------------------------------------------- sliding window
+# Reading: key j is allowed for query i iff i - left <= j <= i + right (negative = no
+# limit on that side); "IO感知计算如何重塑Transformer内存优化技术格局" (bxzpzcl.cn), section
+# 高级功能配置, lists sliding-window attention without defining it.
+
+def brute_window_mask(N, causal, L, left, right):
+    rows = []
+    for i in range(N):
+        row = []
+        for j in range(N):
+            keep = True
+            if causal and j > i:
+                keep = False
+            if L is not None and j >= L:
+                keep = False
+            if left >= 0 and i - j > left:
+                keep = False
+            if right >= 0 and j - i > right:
+                keep = False
+            row.append(keep)
+        rows.append(row)
+    return rows
+
+
+@pytest.mark.parametrize("N,d,causal,kpad,window", [
+    (6, 3, False, None, (0, 0)),
+    (7, 2, False, None, (2, 0)),
+    (7, 2, False, None, (0, 3)),
+    (9, 3, False, None, (3, 2)),
+    (9, 3, True, None, (3, 2)),
+    (8, 2, False, 5, (-1, 2)),
+    (8, 2, True, 6, (4, -1)),
+    (150, 2, False, None, (40, 70)),
+])
+def test_window_matches_brute_force(N, d, causal, kpad, window):
+    q, k, v = rnd((N, d), 31), rnd((N, d), 32), rnd((N, d), 33)
+    scale = 0.8
+    O, L = orc.head_forward(q, k, v, scale, causal, None, kpad, window=window)
+    Ob, Lb = brute_forward(q.tolist(), k.tolist(), v.tolist(), float(np.float32(scale)),
+                           brute_window_mask(N, causal, kpad, *window))
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    fin = np.isfinite(Lb)
+    assert np.array_equal(np.isfinite(L), fin)
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+def test_window_zero_attends_to_itself():
+    # Window (0, 0): each query sees only its own key, so O_i = V_i and
+    # LSE_i = scale * q_i . k_i, and dQ = dK = 0 (a single-key softmax is constant).
+    N, d = 37, 6
+    q, k, v, do = (rnd((N, d), s) for s in (41, 42, 43, 44))
+    s = float(np.float32(0.5))
+    r = orc.head_backward(q, k, v, do, 0.5, window=(0, 0))
+    np.testing.assert_allclose(r["O"], v, atol=1e-14)
+    np.testing.assert_allclose(r["LSE"], s * (q * k).sum(axis=1), atol=1e-13)
+    np.testing.assert_allclose(r["dV"], do, atol=1e-14)
+    assert np.abs(r["dQ"]).max() < 1e-13 and np.abs(r["dK"]).max() < 1e-13
+
+
+def test_window_identities():
+    N, d = 90, 8
+    q, k, v, do = (rnd((N, d), s) for s in (51, 52, 53, 54))
+    none = orc.head_backward(q, k, v, do, 0.3)
+    causal = orc.head_backward(q, k, v, do, 0.3, causal=True)
+    for win, ref in (((-1, -1), none), ((N, N), none), ((-1, 0), causal), ((N, 0), causal)):
+        r = orc.head_backward(q, k, v, do, 0.3, window=win)
+        for key in ("O", "LSE", "dQ", "dK", "dV"):
+            np.testing.assert_array_equal(r[key], ref[key])
+
+
+@pytest.mark.parametrize("left,right", [(5, 3), (0, 7), (11, 0), (4, 4)])
+def test_window_rows_are_attention_on_a_key_slice(left, right):
+    # Row i with a window is plain (unmasked) softmax attention over the contiguous keys
+    # max(0, i-left) .. min(N-1, i+right), computed here with torch on each slice.
+    import torch
+    N, d = 40, 5
+    q, k, v = rnd((N, d), 61), rnd((N, d), 62), rnd((N, d), 63)
+    s = float(np.float32(0.9))
+    O, L = orc.head_forward(q, k, v, 0.9, window=(left, right))
+    for i in range(N):
+        lo, hi = max(0, i - left), min(N, i + right + 1)
+        S = s * (torch.tensor(q[i]) @ torch.tensor(k[lo:hi]).T)
+        np.testing.assert_allclose(O[i], (torch.softmax(S, -1) @ torch.tensor(v[lo:hi])).numpy(),
+                                   atol=1e-13)
+        np.testing.assert_allclose(L[i], torch.logsumexp(S, -1).item(), atol=1e-13)
+
+
+def test_window_gradients_match_central_differences():
+    N, d, win = 15, 4, (3, 2)
+    q, k, v, do = (rnd((N, d), s) for s in (71, 72, 73, 74))
+    scale = 0.7
+    r = orc.head_backward(q, k, v, do, scale, window=win)
+
+    def loss(qq, kk, vv):
+        O, _ = orc.head_forward(qq, kk, vv, scale, window=win)
+        return float((do * O).sum())
+
+    rng = np.random.Generator(np.random.PCG64(75))
+    h = 1e-6
+    for idx, g in ((0, r["dQ"]), (1, r["dK"]), (2, r["dV"])):
+        for _ in range(10):
+            i, c = int(rng.integers(N)), int(rng.integers(d))
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[idx][i, c] += h
+            args_m[idx][i, c] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[i, c]) <= 1e-6 * max(1.0, abs(g[i, c])), (idx, i, c)
+
+
+def test_planted_window_off_by_one_is_caught():
+    # A mask that keeps one key too few on the left (j > i - left) must fail the slice pin.
+    N, d, left, right = 20, 3, 4, 2
+    q, k, v = rnd((N, d), 81), rnd((N, d), 82), rnd((N, d), 83)
+    s = float(np.float32(1.0))
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    ok = (j > i - left) & (j <= i + right)
+    S = s * (q @ k.T)
+    S[~ok] = -np.inf
+    P = np.exp(S - S.max(1, keepdims=True))
+    O_bad = (P / P.sum(1, keepdims=True)) @ v
+    O, _ = orc.head_forward(q, k, v, 1.0, window=(left, right))
+    assert np.abs(O_bad - O).max() > 1e-3
