@@ -31,21 +31,29 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd and fwd+bwd (bf16) at 1 GPU + % MFMA peak"
 
 
-def allowed_pairs(N, causal, blockmask, kv_len_b):
-    """Number of allowed (query, key) pairs of one head, from the mask definitions."""
+def allowed_pairs(N, causal, blockmask, kv_len_b, window=None):
+    """Number of allowed (query, key) pairs of one head, from the mask definitions: row i
+    may see keys lo_i <= j < hi_i (causal, padding, sliding window), thinned by the block
+    table."""
     rows = np.arange(N, dtype=np.int64)
-    lim = np.full(N, N, dtype=np.int64)
+    hi = np.full(N, N, dtype=np.int64)
+    lo = np.zeros(N, dtype=np.int64)
     if causal:
-        lim = np.minimum(lim, rows + 1)
+        hi = np.minimum(hi, rows + 1)
     if kv_len_b is not None:
-        lim = np.minimum(lim, int(kv_len_b))
+        hi = np.minimum(hi, int(kv_len_b))
+    if window is not None:
+        if window[0] >= 0:
+            lo = np.maximum(lo, rows - window[0])
+        if window[1] >= 0:
+            hi = np.minimum(hi, rows + window[1] + 1)
     if blockmask is None:
-        return int(lim.sum())
+        return int(np.clip(hi - lo, 0, None).sum())
     nb = blockmask.shape[0]
     total = 0
     for kb in range(nb):
-        lo = kb * 128
-        cover = np.clip(lim - lo, 0, 128)              # keys of block kb below each row's limit
+        b0 = kb * 128
+        cover = np.clip(np.minimum(hi, b0 + 128) - np.maximum(lo, b0), 0, 128)
         kept = blockmask[rows // 128, kb] != 0
         total += int(cover[kept].sum())
     return total
@@ -56,7 +64,7 @@ def workload_pairs(x):
     total = 0
     for b in range(wl.B):
         kv = None if x.kv_len is None else int(x.kv_len[b])
-        total += wl.H * allowed_pairs(wl.N, wl.causal, x.blockmask, kv)
+        total += wl.H * allowed_pairs(wl.N, wl.causal, x.blockmask, kv, wl.window)
     return total
 
 
@@ -97,14 +105,16 @@ class Buffers:
 
     def fwd(self):
         w = self.wl
-        self.fa.fa_fwd_ex(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d,
-                          w.scale, w.causal, self.bm, self.kv)
+        wl, wr = (-1, -1) if w.window is None else w.window
+        self.fa.fa_fwd_window(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d,
+                              w.scale, w.causal, self.bm, self.kv, wl, wr)
 
     def bwd(self):
         w = self.wl
-        self.fa.fa_bwd_ex(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq, self.dk,
-                          self.dv, w.B, w.H, w.N, w.d, w.scale, w.causal, self.bm, self.kv,
-                          self.ws)
+        wl, wr = (-1, -1) if w.window is None else w.window
+        self.fa.fa_bwd_window(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq,
+                              self.dk, self.dv, w.B, w.H, w.N, w.d, w.scale, w.causal, self.bm,
+                              self.kv, wl, wr, self.ws)
 
     def pre(self):
         w = self.wl
@@ -204,8 +214,8 @@ def cpu_baseline(x, heads=4):
     for b, h in sel:
         kv = None if x.kv_len is None else int(x.kv_len[b])
         args = [orc.widen_bf16(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
-        orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv)
-        flop += 14.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv) * wl.d
+        orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv, window=wl.window)
+        flop += 14.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv, wl.window) * wl.d
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -252,7 +262,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
-                   "causal": wl.causal, "mask": wl.mask, "scale": wl.scale,
+                   "causal": wl.causal, "mask": wl.mask, "window": wl.window,
+                   "scale": wl.scale,
                    "allowed_pairs": pairs},
         "fwd_tflops": round(tf_fwd, 2), "fwd_ms": round(ms_fwd, 4),
         "fwd_bwd_tflops": round(tf_step, 2),

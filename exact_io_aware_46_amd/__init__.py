@@ -28,11 +28,14 @@ _F = ctypes.c_float
 _SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P]),
     "fa_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
+    "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _P]),
     "fa_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P,
                        _P]),
+    "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P,
+                           _I, _I, _P, _P]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -107,6 +110,15 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_l
                            _dev_ptr(kv_len, "kv_len"), _stream_ptr(stream)), "fa_fwd_ex")
 
 
+def fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
+                  window_left=-1, window_right=-1, stream=None):
+    _check(lib().fa_fwd_window(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                               _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
+                               int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                               _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
+                               _stream_ptr(stream)), "fa_fwd_window")
+
+
 def fa_bwd_preprocess(o, dO, delta, B, H, N, d, stream=None):
     _check(lib().fa_bwd_preprocess(_dev_ptr(o, "o"), _dev_ptr(dO, "dO"),
                                    _dev_ptr(delta, "delta"), B, H, N, d,
@@ -136,20 +148,36 @@ def fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, bloc
                            _dev_ptr(workspace, "workspace"), _stream_ptr(stream)), "fa_bwd_ex")
 
 
+def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
+                  blockmask=None, kv_len=None, window_left=-1, window_right=-1,
+                  workspace=None, stream=None):
+    _check(lib().fa_bwd_window(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                               _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
+                               _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H,
+                               N, d, float(scale), int(bool(causal)),
+                               _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
+                               int(window_left), int(window_right),
+                               _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
+           "fa_bwd_window")
+
+
 # ------------------------------------------------- allocating convenience layer
 
-def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, stream=None):
-    """q, k, v: bf16 GPU tensors [B, H, N, d]. Returns (o, lse) newly allocated."""
+def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None,
+            stream=None):
+    """q, k, v: bf16 GPU tensors [B, H, N, d]. Returns (o, lse) newly allocated.
+    ``window`` is None or (left, right) (sliding window, negative = no limit)."""
     import torch
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, stream)
+    wl, wr = (-1, -1) if window is None else window
+    fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr, stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, window=None):
     """Returns (dq, dk, dv) newly allocated; allocates the workspace if none is given."""
     import torch
     B, H, N, d = q.shape
@@ -157,6 +185,7 @@ def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=No
         workspace = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
                                 device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len,
-              workspace, stream)
+    wl, wr = (-1, -1) if window is None else window
+    fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len,
+                  wl, wr, workspace, stream)
     return dq, dk, dv

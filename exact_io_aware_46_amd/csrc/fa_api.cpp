@@ -28,6 +28,10 @@ int check_shape(int B, int H, int N, int d) {
   return FA_OK;
 }
 
+// Window bounds: negative = no limit (-1); a bound of N or more allows every key on that
+// side, so it is stored as N (this also keeps every index sum in the kernels in range).
+int clamp_window(int w, int N) { return w < 0 ? -1 : (w > N ? N : w); }
+
 int check_scale(float scale) {
   if (!std::isfinite(scale) || scale == 0.f) return FA_ERR_SCALE;
   return FA_OK;
@@ -62,9 +66,10 @@ const char* fa_strerror(int status) {
   }
 }
 
-int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
-              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
-              const int32_t* kv_len, void* stream) {
+int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                  float* lse, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -85,8 +90,17 @@ int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, 
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
+  p.wl = clamp_window(window_left, N);
+  p.wr = clamp_window(window_right, N);
   if (fa::launch_fwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* stream) {
+  return fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, -1, -1,
+                       stream);
 }
 
 int fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
@@ -116,10 +130,11 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * round_up(rows * 4, kWsAlign);
 }
 
-int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
-              const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
-              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
-              const int32_t* kv_len, void* workspace, void* stream) {
+int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                  const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* workspace, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -152,8 +167,18 @@ int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf1
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
+  p.wl = clamp_window(window_left, N);
+  p.wr = clamp_window(window_right, N);
   if (fa::launch_bwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+              const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+              int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+              const int32_t* kv_len, void* workspace, void* stream) {
+  return fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
+                       kv_len, -1, -1, workspace, stream);
 }
 
 int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,

@@ -137,8 +137,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const float sc = p.scale * kLog2e;
 
   const int nqt = (N + BQ - 1) / BQ;
-  const int qt_begin = p.causal ? k0 / BQ : 0;
-  const int qt_end = k0 < klim ? nqt : qt_begin;  // a fully padded key tile gets no work
+  // Query q sees key j only if q - ll <= j <= q + rl (causal mask and sliding window), so
+  // the tile's keys are seen by queries k0 - rl .. k0 + BKC - 1 + ll at most.
+  const int rl = right_limit(p.causal, p.wr), ll = left_limit(p.wl);
+  const int qt_begin = max(k0 - rl, 0) / BQ;
+  const int qt_end = k0 < klim ? min(nqt, (k0 + BKC - 1 + ll) / BQ + 1)
+                               : qt_begin;  // a fully padded key tile gets no work
 
   auto next_q = [&](int qt) {
     if (p.blockmask)
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         float pv = fast_exp2(s[i] * sc - lv[j]);
         if constexpr (MASKED) {
           const int q = q0 + qloc + j;
-          const bool ok = mykey < klim && (!p.causal || mykey <= q) && q < N;
+          const bool ok = mykey < klim && mykey <= q + rl && mykey >= q - ll && q < N;
           pv = ok ? pv : 0.f;
         }
         s[i] = pv;
@@ -258,8 +262,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   auto run_step = [&](int qt, const char* Qs, const char* dOs, const float* Ls,
                       const float* Ds) {
     const int qw0 = qt * BQ + qh * 32;  // this wave's first query
-    if ((p.causal && kw > qw0 + 31) || kw >= klim || qw0 >= N) return;
-    if ((p.causal && kw + 31 > qw0) || kw + 32 > klim || qw0 + 32 > N)
+    if (kw > qw0 + 31 + rl || kw + 31 < qw0 - ll || kw >= klim || qw0 >= N) return;
+    if (kw + 31 > qw0 + rl || kw < qw0 + 31 - ll || kw + 32 > klim || qw0 + 32 > N)
       step(std::true_type{}, qt, Qs, dOs, Ls, Ds);
     else
       step(std::false_type{}, qt, Qs, dOs, Ls, Ds);
@@ -361,9 +365,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
   int klim = N;
   if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
-  int kend = klim;
-  if (p.causal) kend = min(kend, q0 + BR);
+  // Key j is allowed for query q only if q - ll <= j <= q + rl.
+  const int rl = right_limit(p.causal, p.wr), ll = left_limit(p.wl);
+  const int kend = min(klim, q0 + BR + rl);
   const int nkt = (kend + BC - 1) / BC;
+  const int kt_lo = max(q0 - ll, 0) / BC;
   const int nb = (N + 127) >> 7;
   // Block table rows of the workgroup's two 128-query blocks and of this wave's block.
   const uint8_t* bm0 = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   // exponent: P = exp2(S * scale * log2(e) - LSE * log2(e)).
   const float sc = p.scale * kLog2e;
 
-  int kt = next_tile(0);
+  int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
   // This lane's query row of Q and dO, as B operands of S^T = K Q^T and dP^T = V dO^T;
@@ -430,9 +436,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   // the row-major K tile by transpose loads.
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
-    if (qw >= N || (p.causal && k0 > qw + 31)) return;
+    if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
     if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
-    const bool need_mask = (p.causal && k0 + BC - 1 > qw) || k0 + BC > klim;
+    const bool need_mask = k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim;
     // One 32-key block at a time, so only one block of S and dP is live.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         float pv = fast_exp2(s[i] * sc - lq);
         if (need_mask) {
           const int key = k0 + kb * 32 + acc_row(i, hi);
-          const bool ok = key < klim && (!p.causal || key <= myq);
+          const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
           if (!ok) pv = 0.f;
         }
         dp[i] = pv * (dp[i] + ndq);

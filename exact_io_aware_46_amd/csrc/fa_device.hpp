@@ -160,4 +160,14 @@ __device__ __forceinline__ i16x4 lds_tr4(const void* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds_ptr);
 }
 
+// Limits of the allowed key range around a query q: keys q - left_limit .. q + right_limit.
+// The causal mask is a right limit of 0; a negative window bound means no limit, given as
+// kUnlimited (large enough that no comparison with it can fail, small enough that adding
+// an index to it cannot overflow).
+constexpr int kUnlimited = 1 << 30;
+__device__ __forceinline__ int right_limit(int causal, int wr) {
+  return causal ? 0 : (wr >= 0 ? wr : kUnlimited);
+}
+__device__ __forceinline__ int left_limit(int wl) { return wl >= 0 ? wl : kUnlimited; }
+
 }  // namespace fa

@@ -75,9 +75,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 
   int klim = N;  // keys >= klim are masked for every query (padding and the N tail)
   if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
-  int kend = klim;
-  if (p.causal) kend = min(kend, q0 + BR);
+  // Key j is allowed for query q only if q - ll <= j <= q + rl (causal mask and sliding
+  // window; kUnlimited where a side has no limit).
+  const int rl = right_limit(p.causal, p.wr), ll = left_limit(p.wl);
+  const int kend = min(klim, q0 + BR + rl);
   const int nkt = (kend + BC - 1) / BC;
+  const int kt_lo = max(q0 - ll, 0) / BC;  // first key tile any query of the workgroup sees
   const int nb = (N + 127) >> 7;
   // Block table rows of the workgroup's two 128-query blocks (the second may not exist)
   // and of this wave's block.
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   const float sc = fabsf(p.scale) * kLog2e;
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
 
-  int kt = next_tile(0);
+  int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
   bf16x8 qf[NS];
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   // One key tile: scores, mask, online softmax, O^T += V^T P^T.
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
-    if (qw >= N || (p.causal && k0 > qw + 31)) return;  // nothing allowed for this wave
+    if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;  // nothing allowed
     if (bmw && !bmw[k0 >> 7]) return;                   // block masked for this wave
 
     f32x16 s[KB];
@@ -160,13 +163,13 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
             s[kb]);
     }
 
-    if ((p.causal && k0 + BC - 1 > qw) || k0 + BC > klim) {
+    if (k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + acc_row(i, hi);
-          const bool ok = key < klim && (!p.causal || key <= myq);
+          const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
           if (!ok) s[kb][i] = -kInf;
         }
     }

@@ -17,6 +17,7 @@ struct FwdParams {
   int B, H, N;
   float scale;
   int causal;
+  int wl, wr;  // sliding window: keys q - wl .. q + wr; negative = no limit on that side
 };
 
 struct BwdParams {
@@ -36,6 +37,7 @@ struct BwdParams {
   int B, H, N;
   float scale;
   int causal;
+  int wl, wr;
 };
 
 // Each returns hipSuccess or the launch error.

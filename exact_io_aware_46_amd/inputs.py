@@ -55,6 +55,7 @@ class Workload:
     mask: str = "none"          # "none" | "kpad" | "block"
     density: float = 1.0        # kept fraction of 128x128 blocks for mask == "block"
     seed: int = 0
+    window: tuple | None = None  # sliding window (left, right); negative = no limit
 
     @property
     def scale(self) -> float:
@@ -65,8 +66,9 @@ class Workload:
         return dataclasses.replace(self, N=n, name=f"{self.name}_N{n}")
 
 
-# The five workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer,
-# a BERT-large-shaped padded layer, a long causal head set, and a block-sparse layer.
+# The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
+# BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, and the
+# long head set with a sliding window.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -74,6 +76,10 @@ WORKLOADS = {
     "long_causal_16k": Workload("long_causal_16k", 1, 16, 16384, 128, causal=True, seed=46004),
     "blocksparse_8k": Workload("blocksparse_8k", 2, 8, 8192, 64, mask="block", density=0.25,
                                seed=46005),
+    # Sliding-window (local) causal attention over the long head set: each query sees
+    # itself and the 4095 keys before it.
+    "sliding_window_16k": Workload("sliding_window_16k", 1, 16, 16384, 128, causal=True,
+                                   seed=46006, window=(4095, 0)),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

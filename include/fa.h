@@ -14,6 +14,11 @@
  *
  * Masks (any combination; a key is allowed iff every active mask allows it):
  *   causal     key j allowed for query i iff j <= i;
+ *   window     (window_left, window_right), fa_fwd_window / fa_bwd_window only: key j allowed
+ *              for query i iff i - window_left <= j <= i + window_right; a negative bound means
+ *              no limit on that side. This is the sliding-window (local) attention the page
+ *              "IO感知计算如何重塑Transformer内存优化技术格局" (bxzpzcl.cn) lists among the
+ *              supported options (section 高级功能配置); (-1, 0) equals the causal mask;
  *   blockmask  uint8 table [nb][nb], nb = ceil(N/128): entry [i/128][j/128] != 0 keeps the
  *              128x128 block (block-sparse attention: the report's 研究亮点 item 3 and the
  *              abstract of "FlashAttention: Fast and Memory-Efficient Exact Attention with
@@ -74,6 +79,14 @@ int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, 
               int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
               const int32_t* kv_len, void* stream);
 
+/* Forward with every mask: as fa_fwd_ex, plus a sliding window (window_left, window_right),
+ * negative = no limit on that side; any value is accepted (bounds of N or more allow every key
+ * on that side). Key tiles outside every query's window are never read. */
+int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                  float* lse, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* stream);
+
 /* Backward preprocess: delta[b][h][i] = sum_c dO[b][h][i][c] * O[b][h][i][c], summed in
  * fp32 over the given bf16 O and dO. This is the row statistic D of the softmax gradient
  * dS = P * (dP - D). fa_bwd runs it itself; it is exported for callers that want D. */
@@ -97,6 +110,13 @@ int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf1
               const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
               int B, int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
               const int32_t* kv_len, void* workspace, void* stream);
+
+/* Backward with every mask (key padding and sliding window, as fa_fwd_window). */
+int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                  const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* workspace, void* stream);
 
 /* Static description of a status code. */
 const char* fa_strerror(int status);

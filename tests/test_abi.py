@@ -37,8 +37,9 @@ def lib():
 
 def test_library_exports_exactly_the_header(lib):
     decl = declared_functions()
-    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_preprocess", "fa_bwd_workspace_bytes",
-                    "fa_fwd", "fa_fwd_ex", "fa_strerror"]
+    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_preprocess", "fa_bwd_window",
+                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_ex", "fa_fwd_window",
+                    "fa_strerror"]
     assert exported_functions() == decl
     for name in decl:
         assert hasattr(lib, name)
@@ -137,3 +138,23 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(x, x, x, x, torch.zeros((1, 1, 8)), 1, 1, 8, 64, 0.125, stream=0)
+
+
+def test_window_entry_points_validate_like_the_others(lib):
+    # Same host-side checks as fa_fwd_ex / fa_bwd_ex; any window value is accepted.
+    p = ptrs(9)
+    fwd_args = lambda q, d, scale: (q, p[1], p[2], p[3], p[4], 1, 1, 64, d, scale, 0, None,
+                                    None, 3, -1, None)
+    assert lib.fa_fwd_window(*fwd_args(None, 64, 0.125)) == 1          # FA_ERR_NULL
+    assert lib.fa_fwd_window(*fwd_args(p[0], 96, 0.125)) == 3          # FA_ERR_UNSUPPORTED_D
+    assert lib.fa_fwd_window(*fwd_args(p[0], 64, float("nan"))) == 5   # FA_ERR_SCALE
+    assert lib.fa_fwd_window(*fwd_args(p[0] + 2, 64, 0.125)) == 4     # FA_ERR_ALIGN
+    ws = A + 64 * T_BYTES
+    bwd_args = lambda q, N: (q, p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], 1, 1, N, 64,
+                             0.125, 1, None, None, -1, 7, ws, None)
+    assert lib.fa_bwd_window(*bwd_args(None, 64)) == 1                 # FA_ERR_NULL
+    assert lib.fa_bwd_window(*bwd_args(p[0], 0)) == 2                  # FA_ERR_SHAPE
+    # an output overlapping an input is rejected before any launch
+    alias = (p[0], p[1], p[2], p[3], p[4], p[5], p[0], p[7], p[8], 1, 1, 64, 64, 0.125, 0,
+             None, None, 5, 5, ws, None)
+    assert lib.fa_bwd_window(*alias) == 7                               # FA_ERR_ALIAS

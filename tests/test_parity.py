@@ -18,15 +18,16 @@ from tests.gpu_util import Run, check_all, check_grad, check_lse, check_o, say, 
 pytestmark = pytest.mark.gpu
 
 
-def oracle_all(q, k, v, do, scale, causal=False, bm=None, kv=None):
-    return orc.backward(q, k, v, do, scale, causal, bm, kv)
+def oracle_all(q, k, v, do, scale, causal=False, bm=None, kv=None, window=None):
+    return orc.backward(q, k, v, do, scale, causal, bm, kv, window=window)
 
 
 def run_and_check(q, k, v, do, scale, causal=False, bm=None, kv=None, what="",
-                  o_rel_slack=0.0):
-    say(f"[parity] {what} shape={q.shape} causal={causal} bm={bm is not None} kv={kv}")
-    res = Run(q, k, v, do, scale, causal, bm, kv).result()
-    ref = oracle_all(q, k, v, do, scale, causal, bm, kv)
+                  o_rel_slack=0.0, window=None):
+    say(f"[parity] {what} shape={q.shape} causal={causal} bm={bm is not None} kv={kv} "
+        f"window={window}")
+    res = Run(q, k, v, do, scale, causal, bm, kv, window=window).result()
+    ref = oracle_all(q, k, v, do, scale, causal, bm, kv, window)
     check_all(res, ref, what, o_rel_slack=o_rel_slack)
     return res, ref
 
@@ -231,18 +232,20 @@ def test_workload_full_compare(name):
                   what=name)
 
 
-@pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k"])
+@pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k", "sliding_window_16k"])
 def test_workload_sampled_compare(name):
     wl = inp.WORKLOADS[name]
     x = inp.make_inputs(wl)
     say(f"[parity] {name} (sampled rows + one full head)")
-    res = Run(x.q, x.k, x.v, x.do, wl.scale, wl.causal, x.blockmask, x.kv_len).result()
+    res = Run(x.q, x.k, x.v, x.do, wl.scale, wl.causal, x.blockmask, x.kv_len,
+              window=wl.window).result()
     for key in res:
         assert np.isfinite(res[key]).all(), key
     sel = _sample_rows(wl, 48, wl.seed)
     o_ref, l_ref = orc.forward_rows(x.q, x.k, x.v, wl.scale, sel, wl.causal, x.blockmask,
-                                    x.kv_len)
-    dq_ref = orc.dq_rows(x.q, x.k, x.v, x.do, wl.scale, sel, wl.causal, x.blockmask, x.kv_len)
+                                    x.kv_len, window=wl.window)
+    dq_ref = orc.dq_rows(x.q, x.k, x.v, x.do, wl.scale, sel, wl.causal, x.blockmask, x.kv_len,
+                         window=wl.window)
     idx = tuple(np.array(sel).T)
     check_o(res["O"][idx], o_ref, name)
     check_lse(res["LSE"][idx], l_ref, name)
@@ -252,8 +255,47 @@ def test_workload_sampled_compare(name):
     kv_b = None if x.kv_len is None else int(x.kv_len[b])
     ref = orc.head_backward(orc.widen_bf16(x.q[b, h]), orc.widen_bf16(x.k[b, h]),
                             orc.widen_bf16(x.v[b, h]), orc.widen_bf16(x.do[b, h]), wl.scale,
-                            wl.causal, x.blockmask, kv_b)
+                            wl.causal, x.blockmask, kv_b, window=wl.window)
     check_o(res["O"][b, h], ref["O"], name)
     check_lse(res["LSE"][b, h], ref["LSE"], name)
     for g in ("dQ", "dK", "dV"):
         check_grad(res[g][b, h], ref[g], g, name)
+
+
+# ------------------------------------------------------------- sliding window
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,window,kv,bm", [
+    (300, False, (0, 0), None, None),
+    (300, False, (32, 0), None, None),
+    (300, True, (100, 5), None, None),
+    (300, False, (100, 50), None, None),
+    (257, False, (17, -1), None, None),
+    (257, False, (-1, 5), None, None),
+    (129, False, (300, 300), None, None),
+    (400, False, (200, 130), [400, 250], None),
+    (384, True, (64, 64), None, [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
+])
+def test_sliding_window(d, N, causal, window, kv, bm):
+    B = 1 if kv is None else len(kv)
+    q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=61 + N)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    bmn = None if bm is None else np.array(bm, dtype=np.uint8)
+    run_and_check(q, k, v, do, 0.125, causal, bmn, kvn, what=f"window {window} d={d}",
+                  window=window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_keys_outside_every_window_are_bitwise_invisible(d):
+    """Window (64, 0): rows >= 256 see only keys >= 192, so NaN in keys and values below
+    192 must leave those rows bitwise unchanged (the tiles are never read)."""
+    N = 512
+    q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=67)
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, :192] = 0x7FC0
+    vp[:, :, :192] = 0x7FC0
+    say(f"[bitexact] window poison d={d}")
+    a = Run(q, k, v, None, 0.125, False, backward=False, window=(64, 0))
+    b = Run(q, kp, vp, None, 0.125, False, backward=False, window=(64, 0))
+    assert _bits_equal(a.o[:, :, 256:].contiguous(), b.o[:, :, 256:].contiguous())
+    assert _bits_equal(a.lse[:, :, 256:].contiguous(), b.lse[:, :, 256:].contiguous())
