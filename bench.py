@@ -87,9 +87,9 @@ class Buffers:
         import exact_io_aware_46_amd as fa
         wl = x.wl
 
-        def dev(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
-                torch.bfloat16)
+        def dev(x):
+            dt = torch.float16 if x.dtype == np.float16 else torch.bfloat16
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(dt)
 
         self.wl = wl
         self.q, self.k, self.v, self.do = dev(x.q), dev(x.k), dev(x.v), dev(x.do)
@@ -106,19 +106,21 @@ class Buffers:
     def fwd(self):
         w = self.wl
         wl, wr = (-1, -1) if w.window is None else w.window
-        self.fa.fa_fwd_window(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d,
-                              w.scale, w.causal, self.bm, self.kv, wl, wr)
+        fn = self.fa.fa_fwd_f16 if w.dtype == "f16" else self.fa.fa_fwd_window
+        fn(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
+           self.bm, self.kv, wl, wr)
 
     def bwd(self):
         w = self.wl
         wl, wr = (-1, -1) if w.window is None else w.window
-        self.fa.fa_bwd_window(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq,
-                              self.dk, self.dv, w.B, w.H, w.N, w.d, w.scale, w.causal, self.bm,
-                              self.kv, wl, wr, self.ws)
+        fn = self.fa.fa_bwd_f16 if w.dtype == "f16" else self.fa.fa_bwd_window
+        fn(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq, self.dk, self.dv, w.B,
+           w.H, w.N, w.d, w.scale, w.causal, self.bm, self.kv, wl, wr, self.ws)
 
     def pre(self):
         w = self.wl
-        self.fa.fa_bwd_preprocess(self.o, self.do, self.delta, w.B, w.H, w.N, w.d)
+        fn = self.fa.fa_bwd_preprocess_f16 if w.dtype == "f16" else self.fa.fa_bwd_preprocess
+        fn(self.o, self.do, self.delta, w.B, w.H, w.N, w.d)
 
     def step(self):
         self.fwd()
@@ -213,7 +215,7 @@ def cpu_baseline(x, heads=4):
     t0 = time.perf_counter()
     for b, h in sel:
         kv = None if x.kv_len is None else int(x.kv_len[b])
-        args = [orc.widen_bf16(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
+        args = [orc.as_f64(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
         orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv, window=wl.window)
         flop += 14.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv, wl.window) * wl.d
     dt = time.perf_counter() - t0
@@ -256,10 +258,11 @@ def main():
     tf_step = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
     tf_fwd = fl_fwd / (ms_fwd * 1e-3) / 1e12
     tf_bwd_main = fl_bwd / (ms_bwd_main * 1e-3) / 1e12
+    tn = "fa::F16" if wl.dtype == "f16" else "fa::Bf16"  # kernel template names (profiles)
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
                    "causal": wl.causal, "mask": wl.mask, "window": wl.window,
@@ -270,20 +273,20 @@ def main():
         "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_bwd_pct_mfma_peak": round(100 * tf_step / MFMA_BF16_PEAK_TFLOPS, 2),
         "bwd_ms": round(ms_bwd, 4), "bwd_preprocess_ms": round(ms_pre, 4),
-        "roofline": {"kernel": f"bwd_dkdv_kernel<{wl.d}> + bwd_dq_kernel<{wl.d}> "
+        "roofline": {"kernel": f"bwd_dkdv_kernel<{tn}, {wl.d}> + bwd_dq_kernel<{tn}, {wl.d}, 64> "
                                "(fa_bwd_ex minus fa_bwd_preprocess)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(
                          wl.name, "bwd_kernel",
-                         [f"bwd_dkdv_kernel<{wl.d}>",
-                          f"bwd_dq_kernel<{wl.d}, 64>"])},
-        "roofline_fwd": {"kernel": f"fwd_kernel<{wl.d}>", "bound": "mfma",
+                         [f"bwd_dkdv_kernel<{tn}, {wl.d}>",
+                          f"bwd_dq_kernel<{tn}, {wl.d}, 64>"])},
+        "roofline_fwd": {"kernel": f"fwd_kernel<{tn}, {wl.d}, 64>", "bound": "mfma",
                          "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(wl.name, "fwd_kernel",
-                                                     [f"fwd_kernel<{wl.d}, 64>"])},
+                                                     [f"fwd_kernel<{tn}, {wl.d}, 64>"])},
     }
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf

@@ -36,6 +36,10 @@ _SIGNATURES = {
                        _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P,
                            _I, _I, _P, _P]),
+    "fa_fwd_f16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _P]),
+    "fa_bwd_preprocess_f16": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_bwd_f16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P,
+                        _I, _I, _P, _P]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -161,18 +165,55 @@ def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
            "fa_bwd_window")
 
 
+def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
+               window_left=-1, window_right=-1, stream=None):
+    _check(lib().fa_fwd_f16(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
+                            int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                            _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
+                            _stream_ptr(stream)), "fa_fwd_f16")
+
+
+def fa_bwd_preprocess_f16(o, dO, delta, B, H, N, d, stream=None):
+    _check(lib().fa_bwd_preprocess_f16(_dev_ptr(o, "o"), _dev_ptr(dO, "dO"),
+                                       _dev_ptr(delta, "delta"), B, H, N, d,
+                                       _stream_ptr(stream)), "fa_bwd_preprocess_f16")
+
+
+def fa_bwd_f16(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
+               kv_len=None, window_left=-1, window_right=-1, workspace=None, stream=None):
+    _check(lib().fa_bwd_f16(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
+                            _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N,
+                            d, float(scale), int(bool(causal)),
+                            _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
+                            int(window_left), int(window_right),
+                            _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
+           "fa_bwd_f16")
+
+
 # ------------------------------------------------- allocating convenience layer
+
+def _is_f16(t):
+    import torch
+    if t.dtype == torch.float16:
+        return True
+    if t.dtype == torch.bfloat16:
+        return False
+    raise ValueError(f"tensors must be bfloat16 or float16, got {t.dtype}")
 
 def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None,
             stream=None):
-    """q, k, v: bf16 GPU tensors [B, H, N, d]. Returns (o, lse) newly allocated.
-    ``window`` is None or (left, right) (sliding window, negative = no limit)."""
+    """q, k, v: bf16 or fp16 GPU tensors [B, H, N, d] (one type for all). Returns (o, lse)
+    newly allocated. ``window`` is None or (left, right) (sliding window, negative = no
+    limit)."""
     import torch
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     wl, wr = (-1, -1) if window is None else window
-    fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr, stream)
+    fn = fa_fwd_f16 if _is_f16(q) else fa_fwd_window
+    fn(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr, stream)
     return o, lse
 
 
@@ -186,6 +227,7 @@ def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=No
                                 device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wl, wr = (-1, -1) if window is None else window
-    fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len,
-                  wl, wr, workspace, stream)
+    fn = fa_bwd_f16 if _is_f16(q) else fa_bwd_window
+    fn(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr,
+       workspace, stream)
     return dq, dk, dv

@@ -66,10 +66,14 @@ const char* fa_strerror(int status) {
   }
 }
 
-int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
-                  float* lse, int B, int H, int N, int d, float scale, int causal,
-                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
-                  int window_right, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+             float* lse, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* blockmask, const int32_t* kv_len, int window_left, int window_right,
+             void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -92,8 +96,28 @@ int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16*
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
-  if (fa::launch_fwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_fwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o,
+                  float* lse, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* stream) {
+  return fwd_impl(fa::kBf16, q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len,
+                  window_left, window_right, stream);
+}
+
+int fa_fwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, fa_f16* o, float* lse, int B,
+               int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+               const int32_t* kv_len, int window_left, int window_right, void* stream) {
+  return fwd_impl(fa::kF16, q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len,
+                  window_left, window_right, stream);
 }
 
 int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
@@ -109,8 +133,12 @@ int fa_fwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, flo
   return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, nullptr, stream);
 }
 
-int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
-                      int d, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int pre_impl(int dtype, const uint16_t* o, const uint16_t* dO, float* delta, int B, int H, int N,
+             int d, void* stream) {
   if (!o || !dO || !delta) return FA_ERR_NULL;
   const int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -118,10 +146,24 @@ int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, 
   const size_t tbytes = (size_t)B * H * N * d * 2;
   const Range rd = span(delta, (size_t)B * H * N * 4);
   if (overlap(rd, span(o, tbytes)) || overlap(rd, span(dO, tbytes))) return FA_ERR_ALIAS;
-  if (fa::launch_bwd_preprocess(o, dO, nullptr, delta, nullptr, B * H * N, d, 1.f,
+  if (fa::launch_bwd_preprocess(o, dO, nullptr, delta, nullptr, B * H * N, d, 1.f, dtype,
                                 static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
+                      int d, void* stream) {
+  return pre_impl(fa::kBf16, o, dO, delta, B, H, N, d, stream);
+}
+
+int fa_bwd_preprocess_f16(const fa_f16* o, const fa_f16* dO, float* delta, int B, int H, int N,
+                          int d, void* stream) {
+  return pre_impl(fa::kF16, o, dO, delta, B, H, N, d, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -130,11 +172,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * round_up(rows * 4, kWsAlign);
 }
 
-int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
-                  const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
-                  int B, int H, int N, int d, float scale, int causal,
-                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
-                  int window_right, void* workspace, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+             const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+             uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* blockmask, const int32_t* kv_len, int window_left, int window_right,
+             void* workspace, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -169,8 +215,31 @@ int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
-  if (fa::launch_bwd(p, d, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
+                  const float* lse, const fa_bf16* dO, fa_bf16* dq, fa_bf16* dk, fa_bf16* dv,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                  int window_right, void* workspace, void* stream) {
+  return bwd_impl(fa::kBf16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
+                  blockmask, kv_len, window_left, window_right, workspace, stream);
+}
+
+int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* o,
+               const float* lse, const fa_f16* dO, fa_f16* dq, fa_f16* dk, fa_f16* dv, int B,
+               int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+               const int32_t* kv_len, int window_left, int window_right, void* workspace,
+               void* stream) {
+  return bwd_impl(fa::kF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
+                  blockmask, kv_len, window_left, window_right, workspace, stream);
 }
 
 int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,

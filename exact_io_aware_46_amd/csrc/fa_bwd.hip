@@ -35,7 +35,7 @@ namespace {
 // masked row (LSE = -inf) mapped to +inf, so exp2(s - lse2) = 0 needs no test in the main
 // passes. The main passes take D negated (dsign = -1): the dK/dV pass then starts the dP
 // accumulator at -D and gets dP - D from the matrix unit.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse,
@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     const u32x4 g = ldg16(dO + row * D + c * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc += __uint_as_float(a[w] << 16) * __uint_as_float(g[w] << 16);
-      acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(g[w] & 0xffff0000u);
+      acc += T::lo(a[w]) * T::lo(g[w]);
+      acc += T::hi(a[w]) * T::hi(g[w]);
     }
   }
 #pragma unroll
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // key group sum their dK, dV partials through LDS at the end. Two waves per SIMD let the
 // hardware overlap one wave's exponentials with the other's matrix products. K and V of
 // the tile stay in LDS (row-major, swizzled) for the whole pass.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
   constexpr int BQ = 64;              // queries per step
@@ -223,10 +223,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
-      s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ao),
-                 *reinterpret_cast<const bf16x8*>(sK + bo), s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(dOs + ao),
-                  *reinterpret_cast<const bf16x8*>(sV + bo), dp);
+      s = mfma32(*reinterpret_cast<const typename T::vec8*>(Qs + ao),
+                 *reinterpret_cast<const typename T::vec8*>(sK + bo), s);
+      dp = mfma32(*reinterpret_cast<const typename T::vec8*>(dOs + ao),
+                  *reinterpret_cast<const typename T::vec8*>(sV + bo), dp);
       // Keep the scheduler from hoisting every operand load of the loop to its top.
       if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
@@ -248,14 +248,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         s[i] = pv;
         dp[i] = pv * dp[i];  // dS = P (dP - D)
       }
-      const bf16x8 pa = pack8(s, 8 * half);
-      const bf16x8 da = pack8(dp, 8 * half);
+      const typename T::vec8 pa = pack8<T>(s, 8 * half);
+      const typename T::vec8 da = pack8<T>(dp, 8 * half);
       const int hoffb = half * 16 * ROWB;
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
         const int o0 = hoffb + (t_off0 ^ (j << 6)), o1 = hoffb + (t_off1 ^ (j << 6));
-        acc_dv[j] = mfma32(pa, cat_tr(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
-        acc_dk[j] = mfma32(da, cat_tr(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
+        acc_dv[j] = mfma32(pa, cat_tr<T>(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
+        acc_dk[j] = mfma32(da, cat_tr<T>(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
       }
     }
   };
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         const float dv = acc_dv[j][i] + *reinterpret_cast<const float*>(bufv + slot(j, i));
         if (key < N) {
           const size_t off = hoff + (size_t)key * D + j * 32 + l32;
-          p.dk[off] = (uint16_t)bf16_bits(dk * p.scale);
-          p.dv[off] = (uint16_t)bf16_bits(dv);
+          p.dk[off] = (uint16_t)T::bits(dk * p.scale);
+          p.dv[off] = (uint16_t)T::bits(dv);
         }
       }
   }
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <int D, int BC>
+template <typename T, int D, int BC>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
   // This lane's query row of Q and dO, as B operands of S^T = K Q^T and dP^T = V dO^T;
   // its log2-scaled LSE and D.
-  bf16x8 qf[NS], gf[NS];
+  typename T::vec8 qf[NS], gf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
@@ -414,8 +414,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
       y = ldg16(dO + (size_t)myq * D + 16 * s + 8 * hi);
     }
-    qf[s] = as_bf16x8(x);
-    gf[s] = as_bf16x8(y);
+    qf[s] = as_vec<T>(x);
+    gf[s] = as_vec<T>(y);
   }
   const float lq = myq < N ? p.lse2[(size_t)bh * N + myq] : kInf;  // +inf: P = 0
   const float ndq = myq < N ? p.ndelta[(size_t)bh * N + myq] : 0.f;  // -D
@@ -447,8 +447,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const int off = kbo + (a_off ^ (st << 5));
-        s = mfma32(*reinterpret_cast<const bf16x8*>(sK + off), qf[st], s);
-        dp = mfma32(*reinterpret_cast<const bf16x8*>(sV + off), gf[st], dp);
+        s = mfma32(*reinterpret_cast<const typename T::vec8*>(sK + off), qf[st], s);
+        dp = mfma32(*reinterpret_cast<const typename T::vec8*>(sV + off), gf[st], dp);
         if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -463,12 +463,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const bf16x8 df = pack8(dp, 8 * half);
+        const typename T::vec8 df = pack8<T>(dp, 8 * half);
         const int ho = kbo + half * 16 * ROWB;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
           const int o0 = ho + (t_off0 ^ (j << 6)), o1 = ho + (t_off1 ^ (j << 6));
-          const bf16x8 kf = cat_tr(lds_tr4(sK + o0), lds_tr4(sK + o1));
+          const typename T::vec8 kf = cat_tr<T>(lds_tr4(sK + o0), lds_tr4(sK + o1));
           acc[j] = mfma32(kf, df, acc[j]);
         }
       }
@@ -499,8 +499,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack_bf16(acc[j][4 * g + 0] * p.scale, acc[j][4 * g + 1] * p.scale);
-        w[1] = pack_bf16(acc[j][4 * g + 2] * p.scale, acc[j][4 * g + 3] * p.scale);
+        w[0] = T::pack(acc[j][4 * g + 0] * p.scale, acc[j][4 * g + 1] * p.scale);
+        w[1] = T::pack(acc[j][4 * g + 2] * p.scale, acc[j][4 * g + 3] * p.scale);
         *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g + 4 * hi) = w;
       }
   }
@@ -508,37 +508,48 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
-                                 float* delta, float* lse2, int rows, int d, float dsign,
-                                 hipStream_t stream) {
+template <typename T>
+hipError_t launch_pre_t(const uint16_t* o, const uint16_t* dO, const float* lse, float* delta,
+                        float* lse2, int rows, int d, float dsign, hipStream_t stream) {
   const int rpb = 256 / (d / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
   if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, stream, o, dO, lse, delta,
+    hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), grid, dim3(256), 0, stream, o, dO, lse, delta,
                        lse2, rows, dsign);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, stream, o, dO, lse, delta, lse2,
-                       rows, dsign);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), grid, dim3(256), 0, stream, o, dO, lse, delta,
+                       lse2, rows, dsign);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
+                                 float* delta, float* lse2, int rows, int d, float dsign,
+                                 int dtype, hipStream_t stream) {
+  return dtype == kF16 ? launch_pre_t<F16>(o, dO, lse, delta, lse2, rows, d, dsign, stream)
+                       : launch_pre_t<Bf16>(o, dO, lse, delta, lse2, rows, d, dsign, stream);
+}
+
+template <typename T>
+hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
-  hipError_t e =
-      launch_bwd_preprocess(p.o, p.dO, p.lse, p.ndelta, p.lse2, rows, d, -1.f, stream);
+  hipError_t e = launch_pre_t<T>(p.o, p.dO, p.lse, p.ndelta, p.lse2, rows, d, -1.f, stream);
   if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);
   if (d == 128) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g_kv, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 128>), g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), g_q, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 128, 64>), g_q, dim3(512), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g_kv, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 64>), g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), g_q, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 64, 64>), g_q, dim3(512), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {
+  return dtype == kF16 ? launch_bwd_t<F16>(p, d, stream) : launch_bwd_t<Bf16>(p, d, stream);
 }
 
 }  // namespace fa

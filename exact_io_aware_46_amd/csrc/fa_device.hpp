@@ -22,8 +22,10 @@ constexpr float kInf = __builtin_huge_valf();
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -47,26 +49,57 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+// The two 16-bit element types. Tensors are raw 16-bit patterns in memory; these give
+// the MFMA operand vector, fp32 -> element rounding (to nearest even: one
+// v_cvt_pk_bf16_f32 or v_cvt_pk_f16_f32 per pair) and exact widening of either half of a
+// 32-bit word.
+struct Bf16 {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {  // a in the low half
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return __uint_as_float(w & 0xffff0000u);
+  }
+};
+struct F16 {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ typename T::vec8 as_vec(u32x4 x) {
+  return __builtin_bit_cast(typename T::vec8, x);
 }
 
-// Eight fp32 accumulator elements [base, base+8) -> one bf16x8 MFMA operand.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int base) {
+// Eight fp32 accumulator elements [base, base+8) -> one MFMA operand of element type T.
+template <typename T>
+__device__ __forceinline__ typename T::vec8 pack8(const f32x16& x, int base) {
   u32x4 r;
-  r[0] = pack_bf16(x[base + 0], x[base + 1]);
-  r[1] = pack_bf16(x[base + 2], x[base + 3]);
-  r[2] = pack_bf16(x[base + 4], x[base + 5]);
-  r[3] = pack_bf16(x[base + 6], x[base + 7]);
-  return as_bf16x8(r);
+  r[0] = T::pack(x[base + 0], x[base + 1]);
+  r[1] = T::pack(x[base + 2], x[base + 3]);
+  r[2] = T::pack(x[base + 4], x[base + 5]);
+  r[3] = T::pack(x[base + 6], x[base + 7]);
+  return as_vec<T>(r);
 }
 
 // Combine a per-lane value with the lane 32 positions away (lanes l and l^32).
@@ -82,27 +115,6 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Four rows (same 8 columns) -> eight 64-bit words, word e holding column e of rows 0..3.
-// Used to write a row-major tile into a transposed LDS layout with 8-byte stores.
-__device__ __forceinline__ u32x2 transpose_col(const u32x4 (&rows)[4], int e) {
-  const int w = e >> 1;
-  u32x2 out;
-  if ((e & 1) == 0) {
-    out[0] = (rows[0][w] & 0xffffu) | (rows[1][w] << 16);
-    out[1] = (rows[2][w] & 0xffffu) | (rows[3][w] << 16);
-  } else {
-    out[0] = (rows[0][w] >> 16) | (rows[1][w] & 0xffff0000u);
-    out[1] = (rows[2][w] >> 16) | (rows[3][w] & 0xffff0000u);
-  }
-  return out;
-}
-
-// Transposed tiles are stored as rows of 16-byte chunks; chunk c of row r sits at
-// position c ^ ((r >> 4) & 7). Rows read together by one MFMA operand load (16
-// consecutive rows) share the same XOR, and the 8-byte transposing stores spread over
-// all banks.
-__device__ __forceinline__ int tchunk(int row, int chunk) { return chunk ^ ((row >> 4) & 7); }
 
 // ---------------------------------------------------------------------------------
 // Row-major tiles in LDS with 16-byte chunks XOR-swizzled by row.
@@ -146,8 +158,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 // Two transpose loads (contraction slots 0..3 and 4..7) -> one MFMA operand.
-__device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+template <typename T>
+__device__ __forceinline__ typename T::vec8 cat_tr(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(typename T::vec8,
+                            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // LDS transpose load (8 bytes per lane). Within each group of 16 lanes, output lane i

@@ -30,7 +30,7 @@
 namespace fa {
 namespace {
 
-template <int D, int BC>
+template <typename T, int D, int BC>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;        // contraction steps of the score MFMA
@@ -119,13 +119,13 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
-  bf16x8 qf[NS];
+  typename T::vec8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (myq < N) x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
     x[0] ^= qsign; x[1] ^= qsign; x[2] ^= qsign; x[3] ^= qsign;
-    qf[s] = as_bf16x8(x);
+    qf[s] = as_vec<T>(x);
   }
 
   f32x16 acc[DB];
@@ -158,9 +158,9 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
       s[kb] = zero16();
 #pragma unroll
       for (int st = 0; st < NS; ++st)
-        s[kb] = mfma32(
-            *reinterpret_cast<const bf16x8*>(sK + kb * 32 * ROWB + (k_off ^ (st << 5))), qf[st],
-            s[kb]);
+        s[kb] = mfma32(*reinterpret_cast<const typename T::vec8*>(
+                           sK + kb * 32 * ROWB + (k_off ^ (st << 5))),
+                       qf[st], s[kb]);
     }
 
     if (k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim) {
@@ -210,11 +210,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const bf16x8 pf = pack8(s[kb], 8 * half);
+        const typename T::vec8 pf = pack8<T>(s[kb], 8 * half);
         const int ho = (kb * 32 + 16 * half) * ROWB;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
-          const bf16x8 vf = cat_tr(lds_tr4(sV + ho + (t_off0 ^ (j << 6))),
+          const typename T::vec8 vf = cat_tr<T>(lds_tr4(sV + ho + (t_off0 ^ (j << 6))),
                                    lds_tr4(sV + ho + (t_off1 ^ (j << 6))));
           acc[j] = mfma32(vf, pf, acc[j]);
         }
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack_bf16(acc[j][4 * g + 0] * inv, acc[j][4 * g + 1] * inv);
-        w[1] = pack_bf16(acc[j][4 * g + 2] * inv, acc[j][4 * g + 3] * inv);
+        w[0] = T::pack(acc[j][4 * g + 0] * inv, acc[j][4 * g + 1] * inv);
+        w[1] = T::pack(acc[j][4 * g + 2] * inv, acc[j][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + j * 32 + 8 * g + 4 * hi) = w;
       }
     if (hi == 0)
@@ -258,14 +258,19 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream) {
+template <typename T>
+hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
   const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<128, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<64, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, int d, int dtype, hipStream_t stream) {
+  return dtype == kF16 ? launch_fwd_t<F16>(p, d, stream) : launch_fwd_t<Bf16>(p, d, stream);
 }
 
 }  // namespace fa

@@ -40,12 +40,16 @@ struct BwdParams {
   int wl, wr;
 };
 
+// Element type of the 16-bit tensors.
+constexpr int kBf16 = 0;
+constexpr int kF16 = 1;
+
 // Each returns hipSuccess or the launch error.
-hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, int dtype, hipStream_t stream);
 // delta = dsign * rowsum(dO * O); lse2 = LSE * log2(e) when lse2 is not null.
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
                                  float* delta, float* lse2, int rows, int d, float dsign,
-                                 hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
+                                 int dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream);
 
 }  // namespace fa

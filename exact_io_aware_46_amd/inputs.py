@@ -12,7 +12,8 @@ GPT-2-small-like, long causal, block-sparse); no dataset is read.
 Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
   1. draw Q, K, V, dO in that order with ``standard_normal(dtype=float32)``,
      C-order ``[B][H][N][d]``;
-  2. round each float32 to bf16 with round-to-nearest-even on the bit pattern;
+  2. round each float32 to bf16 with round-to-nearest-even on the bit pattern (or, for an
+     fp16 workload, to IEEE binary16 with numpy's round-to-nearest-even conversion);
   3. then, if the workload has one, draw the mask input:
      key padding: ``integers(128, 513, size=B)`` (valid length per sequence);
      block mask:  all diagonal blocks kept, plus a uniform draw without replacement
@@ -37,6 +38,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return rounded.astype(np.uint16)
 
 
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's conversion rounds to nearest even)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (used by generators and tests to
     look at inputs; both compute paths do their own widening)."""
@@ -56,6 +62,7 @@ class Workload:
     density: float = 1.0        # kept fraction of 128x128 blocks for mask == "block"
     seed: int = 0
     window: tuple | None = None  # sliding window (left, right); negative = no limit
+    dtype: str = "bf16"          # element type of Q, K, V, dO: "bf16" (uint16 bits) or "f16"
 
     @property
     def scale(self) -> float:
@@ -67,8 +74,8 @@ class Workload:
 
 
 # The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
-# BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, and the
-# long head set with a sliding window.
+# BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, the long
+# head set with a sliding window, and the long causal head set in fp16.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -80,6 +87,9 @@ WORKLOADS = {
     # itself and the 4095 keys before it.
     "sliding_window_16k": Workload("sliding_window_16k", 1, 16, 16384, 128, causal=True,
                                    seed=46006, window=(4095, 0)),
+    # The long causal head set in fp16.
+    "long_causal_16k_f16": Workload("long_causal_16k_f16", 1, 16, 16384, 128, causal=True,
+                                    seed=46007, dtype="f16"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -117,10 +127,11 @@ def draw_block_mask(rng: np.random.Generator, n: int, density: float) -> np.ndar
 def make_inputs(wl: Workload, need_do: bool = True) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(wl.seed))
     shape = (wl.B, wl.H, wl.N, wl.d)
-    q = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
-    k = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
-    v = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
-    do = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)) if need_do else None
+    cvt = f32_to_f16 if wl.dtype == "f16" else f32_to_bf16_bits
+    q = cvt(rng.standard_normal(shape, dtype=np.float32))
+    k = cvt(rng.standard_normal(shape, dtype=np.float32))
+    v = cvt(rng.standard_normal(shape, dtype=np.float32))
+    do = cvt(rng.standard_normal(shape, dtype=np.float32)) if need_do else None
     kv_len = None
     blockmask = None
     if wl.mask == "kpad":
@@ -131,8 +142,10 @@ def make_inputs(wl: Workload, need_do: bool = True) -> Inputs:
     return Inputs(wl, q, k, v, do, kv_len, blockmask)
 
 
-def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal") -> tuple:
-    """Small ad-hoc shapes for edge-case tests: returns (q, k, v, do) bf16 bits.
+def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal",
+                  dtype: str = "bf16") -> tuple:
+    """Small ad-hoc shapes for edge-case tests: returns (q, k, v, do) as bf16 bits
+    (uint16) or, with ``dtype="f16"``, as numpy float16 arrays.
     ``dist="normal"`` draws all four from N(0,1); ``"wide"`` draws Q and K from N(0, 3^2)
     (scores spread ~9x wider, so the softmax is far from uniform) and V, dO from N(0,1)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -140,5 +153,6 @@ def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal
     out = []
     for i in range(4):
         sd = 3.0 if (dist == "wide" and i < 2) else 1.0
-        out.append(f32_to_bf16_bits((sd * rng.standard_normal(shape)).astype(np.float32)))
+        x = (sd * rng.standard_normal(shape)).astype(np.float32)
+        out.append(f32_to_f16(x) if dtype == "f16" else f32_to_bf16_bits(x))
     return tuple(out)

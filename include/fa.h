@@ -27,9 +27,15 @@
  *              [0, N]; they are read on the device and not validated on the host.
  * A query row with no allowed key gets O = 0, LSE = -inf, and contributes no gradient.
  *
+ * Element types: every entry point without a suffix takes bfloat16 tensors; the *_f16 entry
+ * points take fp16 (the deployment page lists fp16 and bf16 among the ROCm data types:
+ * "IO感知计算如何重塑Transformer内存优化技术格局", bxzpzcl.cn, section AMD ROCm生态支持). Both
+ * feed the matrix units in that type and accumulate in fp32; P and dS are rounded to the
+ * same type before the second product of each pair, outputs to nearest even.
+ *
  * Data layout and ownership:
- *   q, k, v, o, dO, dq, dk, dv: contiguous [B][H][N][d] bfloat16 (raw bits, uint16),
- *     DEVICE pointers, 16-byte aligned.
+ *   q, k, v, o, dO, dq, dk, dv: contiguous [B][H][N][d] bfloat16 or fp16 (raw bits,
+ *     uint16), DEVICE pointers, 16-byte aligned.
  *   lse, delta: contiguous [B][H][N] float32, DEVICE pointers, 4-byte aligned.
  *   blockmask, kv_len: DEVICE pointers or NULL (NULL = mask not used).
  *   workspace: DEVICE pointer, 256-byte aligned, at least fa_bwd_workspace_bytes() bytes.
@@ -56,6 +62,7 @@ extern "C" {
 #endif
 
 typedef uint16_t fa_bf16; /* raw bfloat16 bits */
+typedef uint16_t fa_f16;  /* raw IEEE binary16 (fp16) bits */
 
 enum fa_status {
   FA_OK = 0,
@@ -117,6 +124,20 @@ int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa
                   int B, int H, int N, int d, float scale, int causal,
                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
                   int window_right, void* workspace, void* stream);
+
+/* fp16 versions, each with every mask (causal, block table, key padding, sliding window):
+ * arguments, layout, ownership and errors as fa_fwd_window, fa_bwd_preprocess and
+ * fa_bwd_window, with fp16 tensors. */
+int fa_fwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, fa_f16* o, float* lse, int B,
+               int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+               const int32_t* kv_len, int window_left, int window_right, void* stream);
+int fa_bwd_preprocess_f16(const fa_f16* o, const fa_f16* dO, float* delta, int B, int H, int N,
+                          int d, void* stream);
+int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* o,
+               const float* lse, const fa_f16* dO, fa_f16* dq, fa_f16* dk, fa_f16* dv, int B,
+               int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
+               const int32_t* kv_len, int window_left, int window_right, void* workspace,
+               void* stream);
 
 /* Static description of a status code. */
 const char* fa_strerror(int status);

@@ -62,7 +62,8 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
 
 
 def as_f64(x: np.ndarray) -> np.ndarray:
-    """Accept either bf16 bit patterns (uint16) or real arrays."""
+    """Accept either bf16 bit patterns (uint16) or real arrays (numpy float16 for fp16
+    inputs, float32, float64); every value is widened exactly."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return widen_bf16(x)

@@ -30,9 +30,10 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def to_dev(bits: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
-        torch.bfloat16)
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> bfloat16 GPU tensor; numpy float16 -> float16 tensor."""
+    dt = torch.float16 if x.dtype == np.float16 else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(dt)
 
 
 def to_bits(t: torch.Tensor) -> np.ndarray:

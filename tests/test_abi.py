@@ -37,9 +37,9 @@ def lib():
 
 def test_library_exports_exactly_the_header(lib):
     decl = declared_functions()
-    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_preprocess", "fa_bwd_window",
-                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_ex", "fa_fwd_window",
-                    "fa_strerror"]
+    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_f16", "fa_bwd_preprocess",
+                    "fa_bwd_preprocess_f16", "fa_bwd_window", "fa_bwd_workspace_bytes",
+                    "fa_fwd", "fa_fwd_ex", "fa_fwd_f16", "fa_fwd_window", "fa_strerror"]
     assert exported_functions() == decl
     for name in decl:
         assert hasattr(lib, name)
@@ -158,3 +158,15 @@ def test_window_entry_points_validate_like_the_others(lib):
     alias = (p[0], p[1], p[2], p[3], p[4], p[5], p[0], p[7], p[8], 1, 1, 64, 64, 0.125, 0,
              None, None, 5, 5, ws, None)
     assert lib.fa_bwd_window(*alias) == 7                               # FA_ERR_ALIAS
+
+
+def test_f16_entry_points_validate_like_the_others(lib):
+    p = ptrs(9)
+    assert lib.fa_fwd_f16(None, p[1], p[2], p[3], p[4], 1, 1, 64, 64, 0.125, 0, None, None,
+                          -1, -1, None) == 1                           # FA_ERR_NULL
+    assert lib.fa_fwd_f16(p[0], p[1], p[2], p[3], p[4], 1, 1, 64, 32, 0.125, 0, None, None,
+                          -1, -1, None) == 3                           # FA_ERR_UNSUPPORTED_D
+    assert lib.fa_bwd_preprocess_f16(p[0], p[1], p[2] + 1, 1, 1, 64, 64, None) == 4  # ALIGN
+    ws = A + 64 * T_BYTES
+    assert lib.fa_bwd_f16(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], 1, 1, 64, 64,
+                          0.0, 0, None, None, -1, -1, ws, None) == 5     # FA_ERR_SCALE

@@ -524,3 +524,11 @@ def test_planted_window_off_by_one_is_caught():
     O_bad = (P / P.sum(1, keepdims=True)) @ v
     O, _ = orc.head_forward(q, k, v, 1.0, window=(left, right))
     assert np.abs(O_bad - O).max() > 1e-3
+
+
+def test_f16_inputs_widen_exactly():
+    # fp16 tensors reach the oracle as numpy float16 arrays: 1, -2, the largest finite
+    # value, the smallest subnormal and pi rounded to binary16.
+    bits = np.array([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x4248], dtype=np.uint16)
+    want = [1.0, -2.0, 65504.0, 2.0 ** -24, 3.140625]
+    np.testing.assert_array_equal(orc.as_f64(bits.view(np.float16)), want)

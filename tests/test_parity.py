@@ -122,8 +122,8 @@ def test_causal_zero_query_lse_indexing(d):
 # ----------------------------------------------------------- bit-exactness
 
 def _bits_equal(a, b):
-    return a.view(torch.int16).equal(b.view(torch.int16)) if a.dtype == torch.bfloat16 \
-        else torch.equal(a.view(torch.int32), b.view(torch.int32))
+    it = torch.int16 if a.element_size() == 2 else torch.int32
+    return torch.equal(a.view(it), b.view(it))
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -232,7 +232,8 @@ def test_workload_full_compare(name):
                   what=name)
 
 
-@pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k", "sliding_window_16k"])
+@pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k", "sliding_window_16k",
+                                  "long_causal_16k_f16"])
 def test_workload_sampled_compare(name):
     wl = inp.WORKLOADS[name]
     x = inp.make_inputs(wl)
@@ -253,8 +254,8 @@ def test_workload_sampled_compare(name):
     b, h = wl.B - 1, wl.H // 2
     say(f"[parity] {name} full head ({b},{h}) oracle")
     kv_b = None if x.kv_len is None else int(x.kv_len[b])
-    ref = orc.head_backward(orc.widen_bf16(x.q[b, h]), orc.widen_bf16(x.k[b, h]),
-                            orc.widen_bf16(x.v[b, h]), orc.widen_bf16(x.do[b, h]), wl.scale,
+    ref = orc.head_backward(orc.as_f64(x.q[b, h]), orc.as_f64(x.k[b, h]),
+                            orc.as_f64(x.v[b, h]), orc.as_f64(x.do[b, h]), wl.scale,
                             wl.causal, x.blockmask, kv_b, window=wl.window)
     check_o(res["O"][b, h], ref["O"], name)
     check_lse(res["LSE"][b, h], ref["LSE"], name)
@@ -299,3 +300,48 @@ def test_keys_outside_every_window_are_bitwise_invisible(d):
     b = Run(q, kp, vp, None, 0.125, False, backward=False, window=(64, 0))
     assert _bits_equal(a.o[:, :, 256:].contiguous(), b.o[:, :, 256:].contiguous())
     assert _bits_equal(a.lse[:, :, 256:].contiguous(), b.lse[:, :, 256:].contiguous())
+
+
+# ------------------------------------------------------------------- fp16
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,window,kv", [
+    (1, False, None, None),
+    (7, True, None, None),
+    (129, False, None, None),
+    (300, True, None, None),
+    (300, False, (40, 20), None),
+    (257, True, None, [257, 100]),
+])
+def test_f16(d, N, causal, window, kv):
+    B = 1 if kv is None else len(kv)
+    q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=71 + N, dtype="f16")
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    run_and_check(q, k, v, do, 0.125, causal, None, kvn, what=f"f16 d={d}", window=window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f16_all_masks_and_negative_scale(d):
+    N = 384
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=79, dtype="f16")
+    bm = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    kv = np.array([384, 200], dtype=np.int32)
+    run_and_check(q, k, v, do, -0.09, True, bm, kv, what=f"f16 all masks d={d}",
+                  window=(150, -1))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f16_deterministic_and_preprocess(d):
+    import exact_io_aware_46_amd as fa
+    N = 333
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=83, dtype="f16")
+    say(f"[bitexact] f16 determinism + preprocess d={d}")
+    a = Run(q, k, v, do, 0.125, True)
+    b = Run(q, k, v, do, 0.125, True)
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+    delta = torch.empty((2, 2, N), dtype=torch.float32, device="cuda")
+    fa.fa_bwd_preprocess_f16(a.o, a.do, delta, 2, 2, N, d)
+    torch.cuda.synchronize()
+    ref = orc.delta(a.o.cpu().numpy(), do)
+    np.testing.assert_allclose(delta.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
