@@ -36,6 +36,17 @@ notes of the repository):
   key j is allowed for query i iff i - left <= j <= i + right, a negative bound meaning
   no limit on that side (so (-1, 0) is the causal mask);
 * the masks compose by logical AND;
+* dropout, which FlashAttention fuses into the kernel ("FlashAttention学习笔记", section
+  分块计算整体流程: the fused operations; the report's backward bullet: nothing of size
+  N x N is stored, so the dropout mask is regenerated), is read as the usual inverted
+  dropout on the attention probabilities: P_drop = P * keep / (1 - p), O = P_drop V, with
+  LSE the statistic of the undropped softmax. keep is drawn from a counter-based
+  generator so that backward can regenerate it: Philox4x32-10 (Salmon, Moraes, Dror and
+  Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), key (seed low 32 bits,
+  seed high 32 bits), counter (j >> 2, i, b * H + h, offset); word j & 3 of the output is
+  r, and the element is kept iff r >= floor(p * 2^32). Backward through the fixed mask:
+  dV = P_drop^T dO, dP = (dO V^T) * keep / (1 - p), D = rowsum(dO * O),
+  dS = P * (dP - D);
 * a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
 * backward is the derivative of the scalar L = sum(dO * O) with respect to Q, K, V:
   dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic, dS = P * (dP - D),
@@ -94,6 +105,51 @@ def allowed(rows: np.ndarray, n_keys: int, causal: bool, blockmask, kv_len_b,
     return ok
 
 
+# ------------------------------------------------------------------ dropout
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)  # key increments (Weyl sequence)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds on arrays of uint32 counter words and a scalar 2x32-bit key.
+    Each round: (hi, lo) of M0*c0 and M1*c2; new counter = (hi1 ^ c1 ^ k0, lo1,
+    hi0 ^ c3 ^ k1, lo0); then the key is bumped by the Weyl constants."""
+    m = np.uint64(0xFFFFFFFF)
+    c = [np.asarray(x, dtype=np.uint64) & m for x in (c0, c1, c2, c3)]
+    k0, k1 = np.uint64(k0) & m, np.uint64(k1) & m
+    for _ in range(10):
+        p0 = np.uint64(_PHILOX_M[0]) * c[0]
+        p1 = np.uint64(_PHILOX_M[1]) * c[2]
+        c = [((p1 >> np.uint64(32)) ^ c[1] ^ k0) & m, p1 & m,
+             ((p0 >> np.uint64(32)) ^ c[3] ^ k1) & m, p0 & m]
+        k0 = (k0 + np.uint64(_PHILOX_W[0])) & m
+        k1 = (k1 + np.uint64(_PHILOX_W[1])) & m
+    return c
+
+
+def dropout_threshold(p: float) -> int:
+    """Elements whose 32-bit draw is below this are dropped: floor(p * 2^32), p being the
+    float32 value the kernels receive."""
+    pf = float(np.float32(p))
+    return int(min(4294967295.0, np.floor(pf * 4294967296.0)))
+
+
+def dropout_keep(rows, n_keys, bh, p, seed, offset):
+    """Boolean [len(rows), n_keys]: True where element (i, j) of head bh is kept."""
+    rows = np.asarray(rows, dtype=np.int64)
+    i = np.broadcast_to(rows[:, None], (rows.size, n_keys))
+    j = np.broadcast_to(np.arange(n_keys, dtype=np.int64)[None, :], (rows.size, n_keys))
+    words = philox4x32_10(j >> 2, i, np.full(i.shape, bh), np.full(i.shape, offset),
+                          seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    r = np.choose((j & 3).astype(np.int64), words)
+    return r >= np.uint64(dropout_threshold(p))
+
+
+def _dropout_scale(p: float) -> float:
+    return 1.0 / (1.0 - float(np.float32(p)))
+
+
 def _scores(Qr, K, s, ok):
     """S = s * Q K^T on the given query rows, -inf where not allowed."""
     S = s * (Qr @ K.T)
@@ -130,8 +186,9 @@ def _head_view(x, b, h):
 
 
 def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
-                 rows=None, panel=DEFAULT_PANEL, window=None):
-    """One head: returns (O[rows], LSE[rows]) in float64."""
+                 rows=None, panel=DEFAULT_PANEL, window=None, dropout=None):
+    """One head: returns (O[rows], LSE[rows]) in float64. ``dropout`` is None or
+    (p, seed, offset, bh) with bh = b * H + h."""
     N = Kh.shape[0]
     s = _scale64(scale)
     rows = np.arange(Qh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -142,13 +199,16 @@ def head_forward(Qh, Kh, Vh, scale, causal=False, blockmask=None, kv_len_b=None,
         S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b, window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
+        if dropout is not None:
+            p, seed, offset, bh = dropout
+            P = P * dropout_keep(rr, N, bh, p, seed, offset) * _dropout_scale(p)
         O[r0:r0 + rr.size] = P @ Vh
         LSE[r0:r0 + rr.size] = lse
     return O, LSE
 
 
 def head_backward(Qh, Kh, Vh, dOh, scale, causal=False, blockmask=None, kv_len_b=None,
-                  panel=DEFAULT_PANEL, window=None):
+                  panel=DEFAULT_PANEL, window=None, dropout=None):
     """One head, all rows: returns dict with O, LSE, D, dQ, dK, dV (float64)."""
     N, d = Kh.shape
     s = _scale64(scale)
@@ -160,17 +220,25 @@ def head_backward(Qh, Kh, Vh, dOh, scale, causal=False, blockmask=None, kv_len_b
         S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b, window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
-        O = P @ Vh
+        if dropout is None:
+            Pd, keep_scale = P, None
+        else:
+            p, seed, offset, bh = dropout
+            keep_scale = dropout_keep(rr, N, bh, p, seed, offset) * _dropout_scale(p)
+            Pd = P * keep_scale
+        O = Pd @ Vh
         dO = dOh[rr]
         D = (dO * O).sum(axis=1)
         dP = dO @ Vh.T
+        if keep_scale is not None:
+            dP = dP * keep_scale
         dS = P * (dP - D[:, None])
         out["O"][rr] = O
         out["LSE"][rr] = lse
         out["D"][rr] = D
         out["dQ"][rr] = s * (dS @ Kh)
         out["dK"] += s * (dS.T @ Qh[rr])
-        out["dV"] += P.T @ dO
+        out["dV"] += Pd.T @ dO
     return out
 
 
@@ -178,7 +246,12 @@ def _kv_len_b(kv_len, b):
     return None if kv_len is None else int(np.asarray(kv_len)[b])
 
 
-def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None):
+def _head_dropout(dropout, b, h, H):
+    return None if dropout is None else (dropout[0], dropout[1], dropout[2], b * H + h)
+
+
+def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None,
+            dropout=None):
     """All heads. q, k, v: [B][H][N][d] (bf16 bits or reals). Returns O, LSE (float64)."""
     B, H, N, d = q.shape
     O = np.zeros((B, H, N, d))
@@ -187,11 +260,13 @@ def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=No
         for h in range(H):
             O[b, h], LSE[b, h] = head_forward(_head_view(q, b, h), _head_view(k, b, h),
                                               _head_view(v, b, h), scale, causal, blockmask,
-                                              _kv_len_b(kv_len, b), window=window)
+                                              _kv_len_b(kv_len, b), window=window,
+                                              dropout=_head_dropout(dropout, b, h, H))
     return O, LSE
 
 
-def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None, window=None):
+def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None, window=None,
+             dropout=None):
     """All heads. Returns dict of float64 arrays: O, LSE, D, dQ, dK, dV."""
     B, H, N, d = q.shape
     res = {key: np.zeros((B, H, N, d)) for key in ("O", "dQ", "dK", "dV")}
@@ -201,30 +276,31 @@ def backward(q, k, v, do, scale, causal=False, blockmask=None, kv_len=None, wind
         for h in range(H):
             r = head_backward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
                               _head_view(do, b, h), scale, causal, blockmask,
-                              _kv_len_b(kv_len, b), window=window)
+                              _kv_len_b(kv_len, b), window=window,
+                              dropout=_head_dropout(dropout, b, h, H))
             for key in res:
                 res[key][b, h] = r[key]
     return res
 
 
 def forward_rows(q, k, v, scale, sel, causal=False, blockmask=None, kv_len=None,
-                 window=None):
+                 window=None, dropout=None):
     """Sampled rows: ``sel`` is a sequence of (b, h, i). Returns O [len, d], LSE [len]."""
-    d = q.shape[3]
+    H, d = q.shape[1], q.shape[3]
     O = np.zeros((len(sel), d))
     LSE = np.zeros(len(sel))
     for n, (b, h, i) in enumerate(sel):
         o, l = head_forward(_head_view(q, b, h), _head_view(k, b, h), _head_view(v, b, h),
                             scale, causal, blockmask, _kv_len_b(kv_len, b), rows=[i],
-                            window=window)
+                            window=window, dropout=_head_dropout(dropout, b, h, H))
         O[n], LSE[n] = o[0], l[0]
     return O, LSE
 
 
 def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None,
-            window=None):
+            window=None, dropout=None):
     """Sampled dQ rows (each row of dQ depends only on its own row of P and dP)."""
-    N, d = q.shape[2], q.shape[3]
+    H, N, d = q.shape[1], q.shape[2], q.shape[3]
     s = _scale64(scale)
     out = np.zeros((len(sel), d))
     for n, (b, h, i) in enumerate(sel):
@@ -234,9 +310,12 @@ def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None,
                     allowed([i], N, causal, blockmask, _kv_len_b(kv_len, b), window))
         lse = _logsumexp_rows(S)
         P = _probs(S, lse)
-        O = P @ Vh
+        hd = _head_dropout(dropout, b, h, H)
+        ks = 1.0 if hd is None else dropout_keep([i], N, hd[3], hd[0], hd[1], hd[2]) * \
+            _dropout_scale(hd[0])
+        O = (P * ks) @ Vh
         D = (dOi * O).sum(axis=1)
-        dP = dOi @ Vh.T
+        dP = (dOi @ Vh.T) * ks
         dS = P * (dP - D[:, None])
         out[n] = (s * (dS @ Kh))[0]
     return out

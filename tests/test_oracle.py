@@ -532,3 +532,100 @@ def test_f16_inputs_widen_exactly():
     bits = np.array([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x4248], dtype=np.uint16)
     want = [1.0, -2.0, 65504.0, 2.0 ** -24, 3.140625]
     np.testing.assert_array_equal(orc.as_f64(bits.view(np.float16)), want)
+
+
+# ------------------------------------------------------------------ dropout
+# Reading (dropout fused, mask regenerated in backward): P_drop = P * keep / (1 - p) with
+# keep from Philox4x32-10 (Salmon et al., SC 2011); see the oracle's header.
+
+def test_philox_known_answer_vectors():
+    # The generator's published known-answer vectors (counter, key -> output).
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+             ((0xffffffff,) * 4, (0xffffffff,) * 2,
+              (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+             ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+              (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1))]
+    for c, k, want in cases:
+        got = orc.philox4x32_10(*[np.array([x]) for x in c], *k)
+        assert [int(w[0]) for w in got] == list(want)
+
+
+def test_dropout_keep_fraction_and_streams():
+    rows = np.arange(256)
+    for p in (0.0, 0.25, 0.75):
+        keep = orc.dropout_keep(rows, 256, 3, p, 1234, 0)
+        n = keep.size
+        frac = keep.mean()
+        sigma = math.sqrt(p * (1 - p) / n) if 0 < p < 1 else 0.0
+        assert abs(frac - (1 - p)) <= 5 * sigma + 1e-12, (p, frac)
+    base = orc.dropout_keep(rows, 256, 3, 0.5, 1234, 0)
+    for other in (orc.dropout_keep(rows, 256, 4, 0.5, 1234, 0),     # another head
+                  orc.dropout_keep(rows, 256, 3, 0.5, 1235, 0),     # another seed
+                  orc.dropout_keep(rows, 256, 3, 0.5, 1234, 1),     # another offset
+                  orc.dropout_keep(rows, 256, 3, 0.5, 1234 + (1 << 32), 0)):  # seed high word
+        diff = (base != other).mean()
+        assert abs(diff - 0.5) < 0.02, diff                           # independent streams
+    assert orc.dropout_keep(rows, 256, 3, 0.999999, 1234, 0).mean() < 1e-4
+
+
+def test_dropout_zero_is_no_dropout():
+    N, d = 70, 8
+    q, k, v, do = (rnd((N, d), s) for s in (91, 92, 93, 94))
+    a = orc.head_backward(q, k, v, do, 0.4, causal=True)
+    b = orc.head_backward(q, k, v, do, 0.4, causal=True, dropout=(0.0, 77, 5, 2))
+    for key in ("O", "LSE", "dQ", "dK", "dV", "D"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_dropout_forward_matches_brute_force():
+    N, d, p = 11, 3, 0.3
+    q, k, v = rnd((N, d), 95), rnd((N, d), 96), rnd((N, d), 97)
+    keep = orc.dropout_keep(np.arange(N), N, 1, p, 99, 7)
+    O, L = orc.head_forward(q, k, v, 0.8, dropout=(p, 99, 7, 1))
+    s = float(np.float32(0.8))
+    rp = 1.0 / (1.0 - float(np.float32(p)))
+    for i in range(N):
+        sc = [s * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in range(N)]
+        m = max(sc)
+        z = math.fsum(math.exp(x - m) for x in sc)
+        assert abs(L[i] - (m + math.log(z))) < 1e-12               # LSE ignores dropout
+        for c in range(d):
+            want = rp * math.fsum(math.exp(sc[j] - m) / z * v[j][c] for j in range(N)
+                                  if keep[i, j])
+            assert abs(O[i, c] - want) < 1e-12
+
+
+def test_dropout_gradients_match_central_differences():
+    N, d, drop = 14, 4, (0.35, 2024, 3, 5)
+    q, k, v, do = (rnd((N, d), s) for s in (101, 102, 103, 104))
+    scale = 0.7
+    r = orc.head_backward(q, k, v, do, scale, causal=True, dropout=drop)
+
+    def loss(qq, kk, vv):
+        O, _ = orc.head_forward(qq, kk, vv, scale, causal=True, dropout=drop)
+        return float((do * O).sum())
+
+    rng = np.random.Generator(np.random.PCG64(105))
+    h = 1e-6
+    for idx, g in ((0, r["dQ"]), (1, r["dK"]), (2, r["dV"])):
+        for _ in range(10):
+            i, c = int(rng.integers(N)), int(rng.integers(d))
+            ap = [q.copy(), k.copy(), v.copy()]
+            am = [q.copy(), k.copy(), v.copy()]
+            ap[idx][i, c] += h
+            am[idx][i, c] -= h
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            assert abs(fd - g[i, c]) <= 1e-6 * max(1.0, abs(g[i, c])), (idx, i, c)
+
+
+def test_dropout_delta_two_ways():
+    # D = rowsum(dO * O) equals sum_j P_drop_ij (dO V^T)_ij.
+    N, d, drop = 40, 6, (0.5, 7, 0, 0)
+    q, k, v, do = (rnd((N, d), s) for s in (111, 112, 113, 114))
+    r = orc.head_backward(q, k, v, do, 0.3, dropout=drop)
+    s = float(np.float32(0.3))
+    S = s * (q @ k.T)
+    P = np.exp(S - S.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Pd = P * orc.dropout_keep(np.arange(N), N, 0, 0.5, 7, 0) * 2.0
+    np.testing.assert_allclose(r["D"], (Pd * (do @ v.T)).sum(1), atol=1e-12)
