@@ -102,10 +102,16 @@ class Buffers:
         self.bm = None if x.blockmask is None else torch.from_numpy(x.blockmask).cuda()
         self.kv = None if x.kv_len is None else torch.from_numpy(x.kv_len).cuda()
         self.fa = fa
+        self.dtype_code = fa.DTYPE_F16 if wl.dtype == "f16" else fa.DTYPE_BF16
 
     def fwd(self):
         w = self.wl
         wl, wr = (-1, -1) if w.window is None else w.window
+        if w.dropout is not None:
+            self.fa.fa_fwd_dropout(self.dtype_code, self.q, self.k, self.v, self.o, self.lse,
+                                   w.B, w.H, w.N, w.d, w.scale, w.causal, self.bm, self.kv,
+                                   wl, wr, *w.dropout)
+            return
         fn = self.fa.fa_fwd_f16 if w.dtype == "f16" else self.fa.fa_fwd_window
         fn(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
            self.bm, self.kv, wl, wr)
@@ -113,6 +119,12 @@ class Buffers:
     def bwd(self):
         w = self.wl
         wl, wr = (-1, -1) if w.window is None else w.window
+        if w.dropout is not None:
+            self.fa.fa_bwd_dropout(self.dtype_code, self.q, self.k, self.v, self.o, self.lse,
+                                   self.do, self.dq, self.dk, self.dv, w.B, w.H, w.N, w.d,
+                                   w.scale, w.causal, self.bm, self.kv, wl, wr, *w.dropout,
+                                   workspace=self.ws)
+            return
         fn = self.fa.fa_bwd_f16 if w.dtype == "f16" else self.fa.fa_bwd_window
         fn(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq, self.dk, self.dv, w.B,
            w.H, w.N, w.d, w.scale, w.causal, self.bm, self.kv, wl, wr, self.ws)
@@ -216,7 +228,9 @@ def cpu_baseline(x, heads=4):
     for b, h in sel:
         kv = None if x.kv_len is None else int(x.kv_len[b])
         args = [orc.as_f64(t[b, h]) for t in (x.q, x.k, x.v, x.do)]
-        orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv, window=wl.window)
+        drop = None if wl.dropout is None else (*wl.dropout, b * wl.H + h)
+        orc.head_backward(*args, wl.scale, wl.causal, x.blockmask, kv, window=wl.window,
+                          dropout=drop)
         flop += 14.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv, wl.window) * wl.d
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
@@ -258,7 +272,12 @@ def main():
     tf_step = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
     tf_fwd = fl_fwd / (ms_fwd * 1e-3) / 1e12
     tf_bwd_main = fl_bwd / (ms_bwd_main * 1e-3) / 1e12
-    tn = "fa::F16" if wl.dtype == "f16" else "fa::Bf16"  # kernel template names (profiles)
+    # Kernel template names as the profiler prints them.
+    tn = "fa::F16" if wl.dtype == "f16" else "fa::Bf16"
+    dr = "true" if wl.dropout is not None and wl.dropout[0] > 0 else "false"
+    k_dkdv = f"bwd_dkdv_kernel<{tn}, {wl.d}, {dr}>"
+    k_dq = f"bwd_dq_kernel<{tn}, {wl.d}, 64, {dr}>"
+    k_fwd = f"fwd_kernel<{tn}, {wl.d}, 64, {dr}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -266,6 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
                    "causal": wl.causal, "mask": wl.mask, "window": wl.window,
+                   "dropout": None if wl.dropout is None else wl.dropout[0],
                    "scale": wl.scale,
                    "allowed_pairs": pairs},
         "fwd_tflops": round(tf_fwd, 2), "fwd_ms": round(ms_fwd, 4),
@@ -273,20 +293,16 @@ def main():
         "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_bwd_pct_mfma_peak": round(100 * tf_step / MFMA_BF16_PEAK_TFLOPS, 2),
         "bwd_ms": round(ms_bwd, 4), "bwd_preprocess_ms": round(ms_pre, 4),
-        "roofline": {"kernel": f"bwd_dkdv_kernel<{tn}, {wl.d}> + bwd_dq_kernel<{tn}, {wl.d}, 64> "
-                               "(fa_bwd_ex minus fa_bwd_preprocess)",
+        "roofline": {"kernel": f"{k_dkdv} + {k_dq} (backward minus its preprocess)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(
-                         wl.name, "bwd_kernel",
-                         [f"bwd_dkdv_kernel<{tn}, {wl.d}>",
-                          f"bwd_dq_kernel<{tn}, {wl.d}, 64>"])},
-        "roofline_fwd": {"kernel": f"fwd_kernel<{tn}, {wl.d}, 64>", "bound": "mfma",
+                         wl.name, "bwd_kernel", [k_dkdv, k_dq])},
+        "roofline_fwd": {"kernel": k_fwd, "bound": "mfma",
                          "achieved": round(tf_fwd, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(wl.name, "fwd_kernel",
-                                                     [f"fwd_kernel<{tn}, {wl.d}, 64>"])},
+                         "traffic": measured_traffic(wl.name, "fwd_kernel", [k_fwd])},
     }
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf

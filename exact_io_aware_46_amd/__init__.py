@@ -17,13 +17,17 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED_D",
-                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_LAUNCH", 7: "FA_ERR_ALIAS"}
+                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_LAUNCH", 7: "FA_ERR_ALIAS",
+                8: "FA_ERR_DROPOUT", 9: "FA_ERR_DTYPE"}
+DTYPE_BF16, DTYPE_F16 = 0, 1
 
 _lib = None
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
 
 _SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P]),
@@ -40,6 +44,10 @@ _SIGNATURES = {
     "fa_bwd_preprocess_f16": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_bwd_f16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P,
                         _I, _I, _P, _P]),
+    "fa_fwd_dropout": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _I, _I, _F,
+                            _U64, _U32, _P]),
+    "fa_bwd_dropout": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
+                            _P, _I, _I, _F, _U64, _U32, _P, _P]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -192,6 +200,30 @@ def fa_bwd_f16(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blo
            "fa_bwd_f16")
 
 
+def fa_fwd_dropout(dtype, q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None,
+                   kv_len=None, window_left=-1, window_right=-1, dropout_p=0.0, seed=0,
+                   offset=0, stream=None):
+    _check(lib().fa_fwd_dropout(int(dtype), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                _dev_ptr(v, "v"), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H,
+                                N, d, float(scale), int(bool(causal)),
+                                _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
+                                int(window_left), int(window_right), float(dropout_p),
+                                int(seed), int(offset), _stream_ptr(stream)), "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
+                   blockmask=None, kv_len=None, window_left=-1, window_right=-1,
+                   dropout_p=0.0, seed=0, offset=0, workspace=None, stream=None):
+    _check(lib().fa_bwd_dropout(int(dtype), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
+                                _dev_ptr(v, "v"), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"),
+                                _dev_ptr(dO, "dO"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
+                                _dev_ptr(dv, "dv"), B, H, N, d, float(scale), int(bool(causal)),
+                                _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
+                                int(window_left), int(window_right), float(dropout_p),
+                                int(seed), int(offset), _dev_ptr(workspace, "workspace"),
+                                _stream_ptr(stream)), "fa_bwd_dropout")
+
+
 # ------------------------------------------------- allocating convenience layer
 
 def _is_f16(t):
@@ -203,22 +235,26 @@ def _is_f16(t):
     raise ValueError(f"tensors must be bfloat16 or float16, got {t.dtype}")
 
 def forward(q, k, v, scale, causal=False, blockmask=None, kv_len=None, window=None,
-            stream=None):
+            stream=None, dropout=None):
     """q, k, v: bf16 or fp16 GPU tensors [B, H, N, d] (one type for all). Returns (o, lse)
     newly allocated. ``window`` is None or (left, right) (sliding window, negative = no
-    limit)."""
+    limit); ``dropout`` is None or (p, seed, offset)."""
     import torch
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     wl, wr = (-1, -1) if window is None else window
+    if dropout is not None:
+        fa_fwd_dropout(DTYPE_F16 if _is_f16(q) else DTYPE_BF16, q, k, v, o, lse, B, H, N, d,
+                       scale, causal, blockmask, kv_len, wl, wr, *dropout, stream=stream)
+        return o, lse
     fn = fa_fwd_f16 if _is_f16(q) else fa_fwd_window
     fn(q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr, stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=None,
-             workspace=None, stream=None, window=None):
+             workspace=None, stream=None, window=None, dropout=None):
     """Returns (dq, dk, dv) newly allocated; allocates the workspace if none is given."""
     import torch
     B, H, N, d = q.shape
@@ -227,6 +263,11 @@ def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=No
                                 device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wl, wr = (-1, -1) if window is None else window
+    if dropout is not None:
+        fa_bwd_dropout(DTYPE_F16 if _is_f16(q) else DTYPE_BF16, q, k, v, o, lse, dO, dq, dk,
+                       dv, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr, *dropout,
+                       workspace=workspace, stream=stream)
+        return dq, dk, dv
     fn = fa_bwd_f16 if _is_f16(q) else fa_bwd_window
     fn(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr,
        workspace, stream)

@@ -1,5 +1,6 @@
 // C-ABI front end of libfa: argument validation, workspace layout, kernel dispatch.
 // All checks run on the host before any HIP call; nothing is allocated here.
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -32,6 +33,20 @@ int check_shape(int B, int H, int N, int d) {
 // side, so it is stored as N (this also keeps every index sum in the kernels in range).
 int clamp_window(int w, int N) { return w < 0 ? -1 : (w > N ? N : w); }
 
+// Dropout parameters: drop an element iff its 32-bit Philox word is below
+// floor(p * 2^32); scale kept probabilities by 1 / (1 - p). p = 0 selects the kernels
+// without dropout.
+int set_dropout(float p, uint64_t seed, uint32_t offset, uint32_t* t, float* rp, uint32_t* slo,
+                uint32_t* shi, uint32_t* off) {
+  if (!(p >= 0.f && p < 1.f)) return FA_ERR_DROPOUT;
+  *t = (uint32_t)std::min(4294967295.0, std::floor((double)p * 4294967296.0));
+  *rp = 1.f / (1.f - p);
+  *slo = (uint32_t)(seed & 0xFFFFFFFFu);
+  *shi = (uint32_t)(seed >> 32);
+  *off = offset;
+  return FA_OK;
+}
+
 int check_scale(float scale) {
   if (!std::isfinite(scale) || scale == 0.f) return FA_ERR_SCALE;
   return FA_OK;
@@ -62,6 +77,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_SCALE: return "scale must be finite and nonzero";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
+    case FA_ERR_DTYPE: return "unknown element type (0 = bfloat16, 1 = fp16)";
     default: return "unknown status";
   }
 }
@@ -73,7 +90,7 @@ namespace {
 int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
              float* lse, int B, int H, int N, int d, float scale, int causal,
              const uint8_t* blockmask, const int32_t* kv_len, int window_left, int window_right,
-             void* stream) {
+             float dropout_p, uint64_t seed, uint32_t offset, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -96,6 +113,9 @@ int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
+  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_t, &p.drop_rp, &p.seed_lo,
+                        &p.seed_hi, &p.drop_offset)) != FA_OK)
+    return st;
   if (fa::launch_fwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
@@ -110,14 +130,14 @@ int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16*
                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
                   int window_right, void* stream) {
   return fwd_impl(fa::kBf16, q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len,
-                  window_left, window_right, stream);
+                  window_left, window_right, 0.f, 0, 0, stream);
 }
 
 int fa_fwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, fa_f16* o, float* lse, int B,
                int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
                const int32_t* kv_len, int window_left, int window_right, void* stream) {
   return fwd_impl(fa::kF16, q, k, v, o, lse, B, H, N, d, scale, causal, blockmask, kv_len,
-                  window_left, window_right, stream);
+                  window_left, window_right, 0.f, 0, 0, stream);
 }
 
 int fa_fwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16* o, float* lse,
@@ -180,7 +200,7 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
              const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
              uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
              const uint8_t* blockmask, const int32_t* kv_len, int window_left, int window_right,
-             void* workspace, void* stream) {
+             float dropout_p, uint64_t seed, uint32_t offset, void* workspace, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -215,6 +235,9 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
+  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_t, &p.drop_rp, &p.seed_lo,
+                        &p.seed_hi, &p.drop_offset)) != FA_OK)
+    return st;
   if (fa::launch_bwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
@@ -230,7 +253,7 @@ int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa
                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
                   int window_right, void* workspace, void* stream) {
   return bwd_impl(fa::kBf16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
-                  blockmask, kv_len, window_left, window_right, workspace, stream);
+                  blockmask, kv_len, window_left, window_right, 0.f, 0, 0, workspace, stream);
 }
 
 int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* o,
@@ -239,7 +262,7 @@ int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* 
                const int32_t* kv_len, int window_left, int window_right, void* workspace,
                void* stream) {
   return bwd_impl(fa::kF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
-                  blockmask, kv_len, window_left, window_right, workspace, stream);
+                  blockmask, kv_len, window_left, window_right, 0.f, 0, 0, workspace, stream);
 }
 
 int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,
@@ -248,6 +271,34 @@ int fa_bwd_ex(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf1
               const int32_t* kv_len, void* workspace, void* stream) {
   return fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
                        kv_len, -1, -1, workspace, stream);
+}
+
+static int dtype_ok(int dtype) { return dtype == fa::kBf16 || dtype == fa::kF16; }
+
+int fa_fwd_dropout(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                   int window_right, float dropout_p, uint64_t seed, uint32_t offset,
+                   void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  return fwd_impl(dtype, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                  static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d,
+                  scale, causal, blockmask, kv_len, window_left, window_right, dropout_p, seed,
+                  offset, stream);
+}
+
+int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int N, int d, float scale, int causal, const uint8_t* blockmask,
+                   const int32_t* kv_len, int window_left, int window_right, float dropout_p,
+                   uint64_t seed, uint32_t offset, void* workspace, void* stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
+  return bwd_impl(dtype, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                  static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse,
+                  static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
+                  static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d, scale,
+                  causal, blockmask, kv_len, window_left, window_right, dropout_p, seed, offset,
+                  workspace, stream);
 }
 
 int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* o,

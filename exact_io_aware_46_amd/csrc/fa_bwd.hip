@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // key group sum their dK, dV partials through LDS at the end. Two waves per SIMD let the
 // hardware overlap one wave's exponentials with the other's matrix products. K and V of
 // the tile stay in LDS (row-major, swizzled) for the whole pass.
-template <typename T, int D>
+template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
   constexpr int BQ = 64;              // queries per step
@@ -117,6 +117,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const int hi = lane >> 5;
   const int grp = lane >> 4;
   const int t16 = lane & 15;
+  const int qpos = lane & 3;  // position in the quad of lanes (dropout word exchange)
 
   const size_t hoff = (size_t)bh * N * D;
   const uint16_t* __restrict__ Q = p.q + hoff;
@@ -210,16 +211,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     const int q0 = qt * BQ;
     // dP starts at -D of each query row (accumulator element i of lane half hi belongs to
     // query 16*(i/8) + 8*hi + i%8 of this wave's 32), so the products add dO V^T to it.
-    f32x16 s = zero16(), dp;
+    // With dropout dP = (dO V^T) keep / (1 - p) must be masked first, so it starts at 0.
+    f32x16 s = zero16(), dp, nd;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int qloc = qh * 32 + 16 * half + 8 * hi;
       const float4 ga = *reinterpret_cast<const float4*>(&Ds[qloc]);
       const float4 gb = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
-      dp[8 * half + 0] = ga.x; dp[8 * half + 1] = ga.y; dp[8 * half + 2] = ga.z;
-      dp[8 * half + 3] = ga.w; dp[8 * half + 4] = gb.x; dp[8 * half + 5] = gb.y;
-      dp[8 * half + 6] = gb.z; dp[8 * half + 7] = gb.w;
+      nd[8 * half + 0] = ga.x; nd[8 * half + 1] = ga.y; nd[8 * half + 2] = ga.z;
+      nd[8 * half + 3] = ga.w; nd[8 * half + 4] = gb.x; nd[8 * half + 5] = gb.y;
+      nd[8 * half + 6] = gb.z; nd[8 * half + 7] = gb.w;
     }
+    if constexpr (DROP) dp = zero16();
+    else dp = nd;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
@@ -229,6 +233,23 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
                   *reinterpret_cast<const typename T::vec8*>(sV + bo), dp);
       // Keep the scheduler from hoisting every operand load of the loop to its top.
       if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // Dropout words of this lane's key for its 16 queries: the quad of lanes holding keys
+    // 4*(mykey/4) .. +3 shares one Philox call per query; lane c computes the calls of
+    // queries 4*s + c (s = 0..3) and a quad transpose hands every lane its own word.
+    uint32_t kwd[DROP ? 16 : 1];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int sg = 0; sg < 4; ++sg) {
+        const int i = 4 * sg + qpos;
+        const int q = q0 + qh * 32 + 16 * (i >> 3) + 8 * hi + (i & 7);
+        const u32x4 w = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)q, (uint32_t)bh,
+                                      p.drop_offset, p.seed_lo, p.seed_hi);
+        uint32_t r[4] = {w[0], w[1], w[2], w[3]};
+        quad_transpose(r, qpos);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kwd[4 * sg + k] = r[k];
+      }
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -245,8 +266,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
           const bool ok = mykey < klim && mykey <= q + rl && mykey >= q - ll && q < N;
           pv = ok ? pv : 0.f;
         }
-        s[i] = pv;
-        dp[i] = pv * dp[i];  // dS = P (dP - D)
+        if constexpr (DROP) {
+          const bool keep = kwd[i] >= p.drop_t;
+          s[i] = keep ? pv * p.drop_rp : 0.f;                    // P_drop, for dV
+          dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + nd[i]);  // dS = P (dP - D)
+        } else {
+          s[i] = pv;
+          dp[i] = pv * dp[i];  // dS = P (dP - D)
+        }
       }
       const typename T::vec8 pa = pack8<T>(s, 8 * half);
       const typename T::vec8 da = pack8<T>(dp, 8 * half);
@@ -324,7 +351,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <typename T, int D, int BC>
+template <typename T, int D, int BC, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;
@@ -451,6 +478,19 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         dp = mfma32(*reinterpret_cast<const typename T::vec8*>(sV + off), gf[st], dp);
         if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
+      // Dropout words: element i is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8; one Philox
+      // call covers four consecutive keys of this lane's query.
+      uint32_t kwd[DROP ? 16 : 1];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int key0 = k0 + kb * 32 + 16 * (g >> 1) + 8 * hi + 4 * (g & 1);
+          const u32x4 w = philox4x32_10((uint32_t)key0 >> 2, (uint32_t)myq, (uint32_t)bh,
+                                        p.drop_offset, p.seed_lo, p.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kwd[8 * (g >> 1) + 4 * (g & 1) + e] = w[e];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = fast_exp2(s[i] * sc - lq);
@@ -459,7 +499,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
           if (!ok) pv = 0.f;
         }
-        dp[i] = pv * (dp[i] + ndq);
+        if constexpr (DROP) {
+          const bool keep = kwd[i] >= p.drop_t;
+          dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + ndq);  // dS = P (dP - D)
+        } else {
+          dp[i] = pv * (dp[i] + ndq);
+        }
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -529,7 +574,7 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
                        : launch_pre_t<Bf16>(o, dO, lse, delta, lse2, rows, d, dsign, stream);
 }
 
-template <typename T>
+template <typename T, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
   hipError_t e = launch_pre_t<T>(p.o, p.dO, p.lse, p.ndelta, p.lse2, rows, d, -1.f, stream);
@@ -537,19 +582,23 @@ hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);
   if (d == 128) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 128>), g_kv, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 128, DROP>), g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 128, 64>), g_q, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 128, 64, DROP>), g_q, dim3(512), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 64>), g_kv, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 64, DROP>), g_kv, dim3(512), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 64, 64>), g_q, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, 64, 64, DROP>), g_q, dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {
-  return dtype == kF16 ? launch_bwd_t<F16>(p, d, stream) : launch_bwd_t<Bf16>(p, d, stream);
+  if (p.drop_t != 0)
+    return dtype == kF16 ? launch_bwd_t<F16, true>(p, d, stream)
+                         : launch_bwd_t<Bf16, true>(p, d, stream);
+  return dtype == kF16 ? launch_bwd_t<F16, false>(p, d, stream)
+                       : launch_bwd_t<Bf16, false>(p, d, stream);
 }
 
 }  // namespace fa

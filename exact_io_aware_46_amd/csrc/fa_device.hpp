@@ -174,6 +174,49 @@ __device__ __forceinline__ i16x4 lds_tr4(const void* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds_ptr);
 }
 
+// ------------------------------------------------------------------- dropout
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit
+// products, the high halves xored with the other two counter words and the key, the key
+// bumped by a Weyl constant each round. The dropout mask of element (query i, key j) is
+// word j & 3 of the output for counter (j >> 2, i, b*H + h, offset) and key = seed.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c1 = (uint32_t)p1;
+    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return (u32x4){c0, c1, c2, c3};
+}
+
+// 4x4 transpose of 32-bit values across the 4 lanes of each quad (DPP quad permutes):
+// lane c holds row c in r[0..3] on entry and column c on exit (r[k] = entry r[c] of lane
+// k). Two butterfly rounds, exchanging at lane distance 2, then 1.
+__device__ __forceinline__ void quad_transpose(uint32_t (&r)[4], int quad_pos) {
+  const bool b1 = quad_pos & 2, b0 = quad_pos & 1;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t send = b1 ? r[k] : r[k + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);
+    if (b1) r[k] = recv;
+    else r[k + 2] = recv;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k += 2) {
+    const uint32_t send = b0 ? r[k] : r[k + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    if (b0) r[k] = recv;
+    else r[k + 1] = recv;
+  }
+}
+
 // Limits of the allowed key range around a query q: keys q - left_limit .. q + right_limit.
 // The causal mask is a right limit of 0; a negative window bound means no limit, given as
 // kUnlimited (large enough that no comparison with it can fail, small enough that adding

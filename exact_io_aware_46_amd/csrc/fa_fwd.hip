@@ -30,7 +30,7 @@
 namespace fa {
 namespace {
 
-template <typename T, int D, int BC>
+template <typename T, int D, int BC, bool DROP>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;        // contraction steps of the score MFMA
@@ -202,7 +202,22 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
         s[kb][i] = e;
         lsum += e;
       }
-    l_run += lsum;
+    l_run += lsum;  // the normaliser is that of the undropped softmax
+    if constexpr (DROP) {
+      // Dropout: element i of block kb is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8; one
+      // Philox call covers four consecutive keys of this lane's query.
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int key0 = k0 + kb * 32 + 16 * (g >> 1) + 8 * hi + 4 * (g & 1);
+          const u32x4 w = philox4x32_10((uint32_t)key0 >> 2, (uint32_t)myq, (uint32_t)bh,
+                                        p.drop_offset, p.seed_lo, p.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (w[e] < p.drop_t) s[kb][8 * (g >> 1) + 4 * (g & 1) + e] = 0.f;
+        }
+    }
 
     // O^T += V^T P^T. V^T comes from the row-major V tile through transpose loads: lane
     // t of 16-lane group g reads keys (8*(g/2) + t/4) and (+4), columns 16*(g%2) + 4*(t%4).
@@ -240,7 +255,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 
   const float l_tot = xhalf_sum(l_run);
   if (myq < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if constexpr (DROP) inv *= p.drop_rp;  // kept probabilities are scaled by 1 / (1 - p)
     uint16_t* orow = p.o + hoff + (size_t)myq * D;
 #pragma unroll
     for (int j = 0; j < DB; ++j)
@@ -258,19 +274,23 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 
 }  // namespace
 
-template <typename T>
+template <typename T, bool DROP>
 hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
   const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int dtype, hipStream_t stream) {
-  return dtype == kF16 ? launch_fwd_t<F16>(p, d, stream) : launch_fwd_t<Bf16>(p, d, stream);
+  if (p.drop_t != 0)
+    return dtype == kF16 ? launch_fwd_t<F16, true>(p, d, stream)
+                         : launch_fwd_t<Bf16, true>(p, d, stream);
+  return dtype == kF16 ? launch_fwd_t<F16, false>(p, d, stream)
+                       : launch_fwd_t<Bf16, false>(p, d, stream);
 }
 
 }  // namespace fa

@@ -18,6 +18,11 @@ struct FwdParams {
   float scale;
   int causal;
   int wl, wr;  // sliding window: keys q - wl .. q + wr; negative = no limit on that side
+  // Dropout (used only by the kernels built for it): an element is kept iff its Philox
+  // word is >= drop_t; kept probabilities are scaled by drop_rp = 1 / (1 - p).
+  uint32_t drop_t;
+  float drop_rp;
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
 
 struct BwdParams {
@@ -38,6 +43,9 @@ struct BwdParams {
   float scale;
   int causal;
   int wl, wr;
+  uint32_t drop_t;
+  float drop_rp;
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
 
 // Element type of the 16-bit tensors.

@@ -63,6 +63,7 @@ class Workload:
     seed: int = 0
     window: tuple | None = None  # sliding window (left, right); negative = no limit
     dtype: str = "bf16"          # element type of Q, K, V, dO: "bf16" (uint16 bits) or "f16"
+    dropout: tuple | None = None  # attention dropout (p, seed, offset); None = no dropout
 
     @property
     def scale(self) -> float:
@@ -75,7 +76,8 @@ class Workload:
 
 # The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
 # BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, the long
-# head set with a sliding window, and the long causal head set in fp16.
+# head set with a sliding window, the long causal head set in fp16, and the long causal
+# head set with attention dropout.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -90,6 +92,12 @@ WORKLOADS = {
     # The long causal head set in fp16.
     "long_causal_16k_f16": Workload("long_causal_16k_f16", 1, 16, 16384, 128, causal=True,
                                     seed=46007, dtype="f16"),
+    # The long causal head set with dropout p = 0.1 on the attention probabilities (the
+    # pages fix no rate; 0.1 is the customary attention-dropout rate); the Philox seed is
+    # a fixed 64-bit value.
+    "long_causal_16k_dropout": Workload("long_causal_16k_dropout", 1, 16, 16384, 128,
+                                        causal=True, seed=46008,
+                                        dropout=(0.1, 0x5EED_0000_B3D8, 0)),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

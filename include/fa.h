@@ -72,7 +72,9 @@ enum fa_status {
   FA_ERR_ALIGN = 4,          /* a pointer does not have the alignment stated above  */
   FA_ERR_SCALE = 5,          /* scale is zero, NaN or infinite                      */
   FA_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch            */
-  FA_ERR_ALIAS = 7           /* an output buffer overlaps an input or another output */
+  FA_ERR_ALIAS = 7,          /* an output buffer overlaps an input or another output */
+  FA_ERR_DROPOUT = 8,        /* dropout probability not in [0, 1)                    */
+  FA_ERR_DTYPE = 9           /* element type other than 0 (bfloat16) or 1 (fp16)     */
 };
 
 /* Forward. Writes O [B][H][N][d] (bf16) and LSE [B][H][N] (fp32, natural log).
@@ -138,6 +140,29 @@ int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* 
                int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
                const int32_t* kv_len, int window_left, int window_right, void* workspace,
                void* stream);
+
+/* Dropout on the attention probabilities, fused into the kernels and regenerated in the
+ * backward pass (nothing of size N x N is stored): "FlashAttention学习笔记"
+ * (amentiraz.github.io), section 分块计算整体流程, lists dropout among the fused operations,
+ * and the fmread.com report's 算法设计 section says backward recomputes instead of storing.
+ * O = (P * keep / (1 - dropout_p)) V, with LSE the statistic of the undropped softmax.
+ * keep for element (query i, key j) of head (b, h): word j & 3 of Philox4x32-10 (Salmon et
+ * al., SC 2011) with key = seed (low word first) and counter (j >> 2, i, b*H + h, offset);
+ * kept iff the word >= floor(dropout_p * 2^32). The backward must get the same dropout_p,
+ * seed and offset as the forward. dtype: 0 = bfloat16, 1 = fp16 (q, k, v, o, dO, dq, dk, dv
+ * in that type). Every mask as in fa_fwd_window. dropout_p = 0 runs the kernels without
+ * dropout. Errors: FA_ERR_DROPOUT for dropout_p outside [0, 1) or NaN, FA_ERR_DTYPE for an
+ * unknown dtype, otherwise as fa_fwd_window / fa_bwd_window. */
+int fa_fwd_dropout(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+                   int window_right, float dropout_p, uint64_t seed, uint32_t offset,
+                   void* stream);
+int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int N, int d, float scale, int causal, const uint8_t* blockmask,
+                   const int32_t* kv_len, int window_left, int window_right, float dropout_p,
+                   uint64_t seed, uint32_t offset, void* workspace, void* stream);
 
 /* Static description of a status code. */
 const char* fa_strerror(int status);

@@ -50,7 +50,7 @@ class Run:
     """Device buffers and results of one libfa forward + backward."""
 
     def __init__(self, q, k, v, do, scale, causal=False, blockmask=None, kv_len=None,
-                 backward=True, window=None):
+                 backward=True, window=None, dropout=None):
         self.dq_ = self.dk_ = self.dv_ = None
         self.q, self.k, self.v = to_dev(q), to_dev(k), to_dev(v)
         self.do = to_dev(do) if do is not None else None
@@ -60,11 +60,11 @@ class Run:
             np.ascontiguousarray(kv_len, dtype=np.int32)).cuda()
         self.scale, self.causal = scale, causal
         self.o, self.lse = fa.forward(self.q, self.k, self.v, scale, causal, self.bm, self.kv,
-                                      window=window)
+                                      window=window, dropout=dropout)
         if backward:
             self.dq_, self.dk_, self.dv_ = fa.backward(self.q, self.k, self.v, self.o, self.lse,
                                                        self.do, scale, causal, self.bm, self.kv,
-                                                       window=window)
+                                                       window=window, dropout=dropout)
         torch.cuda.synchronize()
 
     def result(self):

@@ -37,16 +37,17 @@ def lib():
 
 def test_library_exports_exactly_the_header(lib):
     decl = declared_functions()
-    assert decl == ["fa_bwd", "fa_bwd_ex", "fa_bwd_f16", "fa_bwd_preprocess",
-                    "fa_bwd_preprocess_f16", "fa_bwd_window", "fa_bwd_workspace_bytes",
-                    "fa_fwd", "fa_fwd_ex", "fa_fwd_f16", "fa_fwd_window", "fa_strerror"]
+    assert decl == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_ex", "fa_bwd_f16",
+                    "fa_bwd_preprocess", "fa_bwd_preprocess_f16", "fa_bwd_window",
+                    "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_dropout", "fa_fwd_ex",
+                    "fa_fwd_f16", "fa_fwd_window", "fa_strerror"]
     assert exported_functions() == decl
     for name in decl:
         assert hasattr(lib, name)
 
 
 def test_strerror(lib):
-    for st in range(8):
+    for st in range(10):
         assert len(fa.strerror(st)) > 0
     assert fa.strerror(99) == "unknown status"
 
@@ -170,3 +171,20 @@ def test_f16_entry_points_validate_like_the_others(lib):
     ws = A + 64 * T_BYTES
     assert lib.fa_bwd_f16(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], 1, 1, 64, 64,
                           0.0, 0, None, None, -1, -1, ws, None) == 5     # FA_ERR_SCALE
+
+
+def test_dropout_entry_points_validate(lib):
+    p = ptrs(9)
+    fwd = lambda dt, pd: lib.fa_fwd_dropout(dt, p[0], p[1], p[2], p[3], p[4], 1, 1, 64, 64,
+                                            0.125, 0, None, None, -1, -1, pd, 7, 0, None)
+    assert fwd(0, 1.0) == 8                     # FA_ERR_DROPOUT: p must be < 1
+    assert fwd(0, -0.25) == 8
+    assert fwd(1, float("nan")) == 8
+    assert fwd(2, 0.1) == 9                     # FA_ERR_DTYPE
+    ws = A + 64 * T_BYTES
+    bwd = lambda dt, pd, q: lib.fa_bwd_dropout(dt, q, p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                                               p[8], 1, 1, 64, 64, 0.125, 0, None, None, -1,
+                                               -1, pd, (1 << 40) + 3, 5, ws, None)
+    assert bwd(0, 0.1, None) == 1               # FA_ERR_NULL
+    assert bwd(5, 0.1, p[0]) == 9
+    assert bwd(1, 1.5, p[0]) == 8

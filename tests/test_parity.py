@@ -345,3 +345,146 @@ def test_f16_deterministic_and_preprocess(d):
     torch.cuda.synchronize()
     ref = orc.delta(a.o.cpu().numpy(), do)
     np.testing.assert_allclose(delta.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ dropout
+
+# Kept probabilities are scaled by 1 / (1-p), so with few keys |O| grows to ~|V| / (1-p);
+# the bf16 rounding of P (operand) and of O (output), 2^-9 relative each, then exceeds
+# the flat 1e-2 bound, which is widened by 2^-7 |O| elementwise.
+DROP_O_SLACK = 2.0 ** -7
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,window,kv,p", [
+    (1, False, None, None, 0.1),
+    (7, True, None, None, 0.5),
+    (129, False, None, None, 0.1),
+    (300, True, None, None, 0.2),
+    (300, False, (40, 20), None, 0.3),
+    (257, True, None, [257, 100], 0.1),
+    (384, False, None, [384, 130], 0.9),
+])
+def test_dropout(d, N, causal, window, kv, p):
+    B = 1 if kv is None else len(kv)
+    q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=89 + N)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    drop = (p, 0x1234_5678_9ABC + N, 3)
+    what = f"dropout p={p} d={d}"
+    say(f"[parity] {what} N={N} causal={causal} window={window} kv={kv}")
+    res = Run(q, k, v, do, 0.125, causal, None, kvn, window=window, dropout=drop).result()
+    ref = orc.backward(q, k, v, do, 0.125, causal, None, kvn, window=window, dropout=drop)
+    if N > 1:
+        check_all(res, ref, what, o_rel_slack=DROP_O_SLACK)
+        return
+    # One key: P = 1, so dS = keep / (1-p) * dP - D cancels exactly in the oracle, which
+    # takes D from its exact O. The kernels take D from the bf16 O they stored, which with
+    # the 1 / (1-p) factor is no longer exact, leaving dS = D_exact - D_stored: then
+    # dQ = scale * dS * k and dK = scale * dS * q, predicted here up to the bf16 rounding
+    # of dS before its product (relative 2^-8) and fp32 noise.
+    check_all(res, ref, what, grads=False, o_rel_slack=DROP_O_SLACK)
+    check_grad(res["dV"], ref["dV"], "dV", what)
+    ds = orc.delta(ref["O"], do) - orc.delta(res["O"], do)
+    for name, x in (("dQ", k), ("dK", q)):
+        pred = ref[name] + 0.125 * ds[..., None] * orc.as_f64(x)
+        err = np.abs(res[name] - pred)
+        assert (err <= 2e-5 + np.abs(pred) / 256).all(), \
+            f"{what} {name} vs predicted residual {err.max():.3e}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_all_masks_f16_and_negative_scale(d):
+    N = 384
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=97, dtype="f16")
+    bm = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    kv = np.array([384, 200], dtype=np.int32)
+    drop = (0.25, (1 << 63) + 12345, 77)
+    say(f"[parity] dropout f16 all masks d={d}")
+    res = Run(q, k, v, do, -0.09, True, bm, kv, window=(150, -1), dropout=drop).result()
+    ref = orc.backward(q, k, v, do, -0.09, True, bm, kv, window=(150, -1), dropout=drop)
+    check_all(res, ref, f"dropout f16 d={d}", o_rel_slack=DROP_O_SLACK)
+
+
+def _identity_rows(B, H, N, d):
+    """bf16 bits of rows e_{j mod d}: row j of every head is the unit vector j mod d."""
+    x = np.zeros((B, H, N, d), dtype=np.float32)
+    j = np.arange(N)
+    x[:, :, j, j % d] = 1.0
+    return inp.f32_to_bf16_bits(x)
+
+
+# Query block r attends to key block PERM[r] only, so each query row sees exactly 128 keys
+# and each key block exactly one query block.
+_PERM_BM = np.array([[0, 1, 0, 0], [1, 0, 0, 0], [0, 0, 0, 1], [0, 0, 1, 0]], dtype=np.uint8)
+
+
+def _perm_keep(H, N, drop):
+    """Oracle keep mask [H][N][128]: column c of row i is key 128 * PERM[i // 128] + c."""
+    keep = np.zeros((H, N, 128), dtype=bool)
+    for h in range(H):
+        full = orc.dropout_keep(np.arange(N), N, h, *drop)
+        for r in range(N // 128):
+            c0 = 128 * int(np.argmax(_PERM_BM[r]))
+            keep[h, 128 * r:128 * (r + 1)] = full[128 * r:128 * (r + 1), c0:c0 + 128]
+    return keep
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_dropout_masks_of_every_kernel_are_bit_exact(p):
+    """Read each kernel's keep mask out of its output and compare it bit for bit with the
+    oracle's Philox mask (d = 128, one 128-key block per query row):
+      forward:   V = I, so O[i, c] is P_drop(i, key c) -- exactly zero iff dropped;
+      dK/dV:     dO = I as well, so dV[key, c] is P_drop(query c, key) -- zero iff dropped;
+      dQ:        K = V = I, so dP(i, key c) = dO[i, c] and
+                 dQ[i, c] = scale * P(i,c) * (keep * dO[i,c] / (1-p) - D_i); with P and D
+                 from the oracle, keep is recovered wherever |dO[i,c]| is not tiny."""
+    B, H, N, d = 1, 2, 512, 128
+    drop = (p, 0xDEAD_BEEF_0042, 5)
+    q, k, v, do = inp.custom_inputs(B, H, N, d, seed=101)
+    eye = _identity_rows(B, H, N, d)
+    keep = _perm_keep(H, N, drop)
+    say(f"[bitexact] dropout masks p={p}: forward and dK/dV")
+    a = Run(q, k, eye, eye, 0.125, False, _PERM_BM, dropout=drop).result()
+    assert np.array_equal(a["O"][0] != 0, keep), "forward keep mask"
+    # dV[key j, c] for key block PERM[r] comes from query 128 r + c.
+    dv_keep = np.zeros_like(keep)
+    for r in range(N // 128):
+        c0 = 128 * int(np.argmax(_PERM_BM[r]))
+        dv_keep[:, 128 * r:128 * (r + 1)] = np.swapaxes(a["dV"][0, :, c0:c0 + 128] != 0, 1, 2)
+    assert np.array_equal(dv_keep, keep), "dK/dV keep mask"
+    say(f"[bitexact] dropout masks p={p}: dQ")
+    b = Run(q, eye, eye, do, 0.125, False, _PERM_BM, dropout=drop).result()
+    ref = orc.backward(q, eye, eye, do, 0.125, False, _PERM_BM, None, dropout=drop)
+    D = orc.delta(ref["O"], orc.as_f64(do))            # rowsum(dO * O) of the dropped O
+    P = np.exp(0.125 * orc.as_f64(q) - ref["LSE"][..., None])[0]   # P(i, key c) = e^(s q_ic - L)
+    dof = orc.as_f64(do)[0]
+    rp = 1.0 / (1.0 - float(np.float32(p)))
+    est = (b["dQ"][0] / (0.125 * P) + D[0][..., None]) / (dof * rp)
+    sure = np.abs(dof) > 0.1
+    assert sure.mean() > 0.85
+    assert np.array_equal((est > 0.5)[sure], keep[sure]), "dQ keep mask"
+    check_all(b, ref, f"dropout K=I p={p}", o_rel_slack=DROP_O_SLACK)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_p0_is_bitwise_no_dropout_and_outputs_deterministic(d):
+    import exact_io_aware_46_amd as fa
+    N = 300
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=103)
+    say(f"[bitexact] dropout p=0 / determinism d={d}")
+    plain = Run(q, k, v, do, 0.125, True)
+    zero = Run(q, k, v, do, 0.125, True, dropout=(0.0, 99, 1))
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(plain, name), getattr(zero, name)), name
+    drop = (0.3, 2024, 9)
+    a = Run(q, k, v, do, 0.125, True, dropout=drop)
+    b = Run(q, k, v, do, 0.125, True, dropout=drop)
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+    # The statistics ignore dropout: LSE is that of the undropped softmax.
+    np.testing.assert_allclose(to_f64(a.lse), to_f64(plain.lse), rtol=0, atol=1e-6)
+    # A new seed or offset draws a new mask.
+    c = Run(q, k, v, do, 0.125, True, dropout=(0.3, 2025, 9), backward=False)
+    e = Run(q, k, v, do, 0.125, True, dropout=(0.3, 2024, 10), backward=False)
+    assert not _bits_equal(a.o, c.o) and not _bits_equal(a.o, e.o)
+    with pytest.raises(fa.FAError):
+        Run(q, k, v, do, 0.125, True, dropout=(1.0, 1, 0), backward=False)
