@@ -43,8 +43,12 @@ notes of the repository):
   LSE the statistic of the undropped softmax. keep is drawn from a counter-based
   generator so that backward can regenerate it: Philox4x32-10 (Salmon, Moraes, Dror and
   Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), key (seed low 32 bits,
-  seed high 32 bits), counter (j >> 2, i, b * H + h, offset); word j & 3 of the output is
-  r, and the element is kept iff r >= floor(p * 2^32). Backward through the fixed mask:
+  seed high 32 bits), counter (j >> 2, i >> 1, b * H + h, offset). One call covers a
+  patch of 2 queries x 4 keys: word j & 3 of the output, its low 16 bits for even i and
+  its high 16 bits for odd i, is the 16-bit draw r, and the element is kept iff
+  r >= floor(p * 2^16) (p resolved to 2^-16; the pages fix no generator, and 16-bit
+  draws halve the generator work per element against 32-bit ones). Backward through the
+  fixed mask:
   dV = P_drop^T dO, dP = (dO V^T) * keep / (1 - p), D = rowsum(dO * O),
   dS = P * (dP - D);
 * a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
@@ -129,10 +133,10 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def dropout_threshold(p: float) -> int:
-    """Elements whose 32-bit draw is below this are dropped: floor(p * 2^32), p being the
+    """Elements whose 16-bit draw is below this are dropped: floor(p * 2^16), p being the
     float32 value the kernels receive."""
     pf = float(np.float32(p))
-    return int(min(4294967295.0, np.floor(pf * 4294967296.0)))
+    return int(min(65535.0, np.floor(pf * 65536.0)))
 
 
 def dropout_keep(rows, n_keys, bh, p, seed, offset):
@@ -140,9 +144,10 @@ def dropout_keep(rows, n_keys, bh, p, seed, offset):
     rows = np.asarray(rows, dtype=np.int64)
     i = np.broadcast_to(rows[:, None], (rows.size, n_keys))
     j = np.broadcast_to(np.arange(n_keys, dtype=np.int64)[None, :], (rows.size, n_keys))
-    words = philox4x32_10(j >> 2, i, np.full(i.shape, bh), np.full(i.shape, offset),
+    words = philox4x32_10(j >> 2, i >> 1, np.full(i.shape, bh), np.full(i.shape, offset),
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    r = np.choose((j & 3).astype(np.int64), words)
+    w = np.choose((j & 3).astype(np.int64), words)
+    r = (w >> (16 * (i & 1)).astype(np.uint64)) & np.uint64(0xFFFF)
     return r >= np.uint64(dropout_threshold(p))
 
 

@@ -568,6 +568,24 @@ def test_dropout_keep_fraction_and_streams():
     assert orc.dropout_keep(rows, 256, 3, 0.999999, 1234, 0).mean() < 1e-4
 
 
+def test_dropout_draw_layout_and_threshold_by_hand():
+    # Element (i, j) of head bh takes the 16-bit half (low for even i, high for odd i) of
+    # output word j % 4 of the call with counter (j // 4, i // 2, bh, offset); it is kept
+    # iff that draw r >= floor(p * 2^16). Worked through for single elements with plain
+    # integers, and p placed on both sides of the boundary r / 2^16.
+    seed, bh, off = 0x0123_4567_89AB_CDEF, 6, 11
+    for i, j in ((0, 0), (1, 0), (5, 13), (6, 13), (200, 77), (201, 78), (37, 255)):
+        words = orc.philox4x32_10(np.array([j // 4]), np.array([i // 2]), np.array([bh]),
+                                  np.array([off]), seed & 0xFFFFFFFF, seed >> 32)
+        word = int(words[j % 4][0])
+        r = (word >> 16) if i % 2 else (word & 0xFFFF)
+        rows = np.array([i])
+        # p exactly r / 2^16 (float32 represents it exactly): floor(p 2^16) = r, kept.
+        assert orc.dropout_keep(rows, j + 1, bh, r / 65536.0, seed, off)[0, j]
+        if r < 65535:   # one step above: threshold r + 1 > r, dropped
+            assert not orc.dropout_keep(rows, j + 1, bh, (r + 1) / 65536.0, seed, off)[0, j]
+
+
 def test_dropout_zero_is_no_dropout():
     N, d = 70, 8
     q, k, v, do = (rnd((N, d), s) for s in (91, 92, 93, 94))
