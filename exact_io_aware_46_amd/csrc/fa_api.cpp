@@ -36,10 +36,11 @@ int clamp_window(int w, int N) { return w < 0 ? -1 : (w > N ? N : w); }
 // Dropout parameters: drop an element iff its 32-bit Philox word is below
 // floor(p * 2^32); scale kept probabilities by 1 / (1 - p). p = 0 selects the kernels
 // without dropout.
-int set_dropout(float p, uint64_t seed, uint32_t offset, uint32_t* t, float* rp, uint32_t* slo,
-                uint32_t* shi, uint32_t* off) {
+int set_dropout(float p, uint64_t seed, uint32_t offset, int* on, uint32_t* t, float* rp,
+                uint32_t* slo, uint32_t* shi, uint32_t* off) {
   if (!(p >= 0.f && p < 1.f)) return FA_ERR_DROPOUT;
-  *t = (uint32_t)std::min(4294967295.0, std::floor((double)p * 4294967296.0));
+  *on = p > 0.f;
+  *t = (uint32_t)std::min(65535.0, std::floor((double)p * 65536.0));
   *rp = 1.f / (1.f - p);
   *slo = (uint32_t)(seed & 0xFFFFFFFFu);
   *shi = (uint32_t)(seed >> 32);
@@ -113,7 +114,7 @@ int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
-  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_t, &p.drop_rp, &p.seed_lo,
+  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_on, &p.drop_t, &p.drop_rp, &p.seed_lo,
                         &p.seed_hi, &p.drop_offset)) != FA_OK)
     return st;
   if (fa::launch_fwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -235,7 +236,7 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.causal = causal ? 1 : 0;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
-  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_t, &p.drop_rp, &p.seed_lo,
+  if ((st = set_dropout(dropout_p, seed, offset, &p.drop_on, &p.drop_t, &p.drop_rp, &p.seed_lo,
                         &p.seed_hi, &p.drop_offset)) != FA_OK)
     return st;
   if (fa::launch_bwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)

@@ -118,6 +118,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const int grp = lane >> 4;
   const int t16 = lane & 15;
   const int qpos = lane & 3;  // position in the quad of lanes (dropout word exchange)
+  [[maybe_unused]] const DropKey dk{(uint32_t)bh, p.drop_offset, p.seed_lo, p.seed_hi};
+  [[maybe_unused]] const uint32_t thi = p.drop_t << 16;
 
   const size_t hoff = (size_t)bh * N * D;
   const uint16_t* __restrict__ Q = p.q + hoff;
@@ -234,17 +236,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       // Keep the scheduler from hoisting every operand load of the loop to its top.
       if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
-    // Dropout words of this lane's key for its 16 queries: the quad of lanes holding keys
-    // 4*(mykey/4) .. +3 shares one Philox call per query; lane c computes the calls of
-    // queries 4*s + c (s = 0..3) and a quad transpose hands every lane its own word.
-    uint32_t kwd[DROP ? 16 : 1];
+    // Dropout draws of this lane's key for its 16 queries (element i is query
+    // q0 + 32*qh + 16*(i/8) + 8*hi + i%8). The quad of lanes holding keys 4*(mykey/4) .. +3
+    // shares one Philox call per query pair (elements 2m, 2m+1); lane c computes the calls
+    // of pairs 4*sg + c (sg = 0, 1) and a quad transpose hands every lane the word of its
+    // key: kwd[m] holds the draws of elements 2m (low half) and 2m+1 (high half).
+    uint32_t kwd[DROP ? 8 : 1];
     if constexpr (DROP) {
 #pragma unroll
-      for (int sg = 0; sg < 4; ++sg) {
-        const int i = 4 * sg + qpos;
-        const int q = q0 + qh * 32 + 16 * (i >> 3) + 8 * hi + (i & 7);
-        const u32x4 w = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)q, (uint32_t)bh,
-                                      p.drop_offset, p.seed_lo, p.seed_hi);
+      for (int sg = 0; sg < 2; ++sg) {
+        const int q = q0 + qh * 32 + 16 * sg + 8 * hi + 2 * qpos;  // even query of the pair
+        const u32x4 w = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)q >> 1, dk.bh,
+                                      dk.offset, dk.seed_lo, dk.seed_hi);
         uint32_t r[4] = {w[0], w[1], w[2], w[3]};
         quad_transpose(r, qpos);
 #pragma unroll
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
           pv = ok ? pv : 0.f;
         }
         if constexpr (DROP) {
-          const bool keep = kwd[i] >= p.drop_t;
+          const bool keep = drop_keep(kwd[i >> 1], i & 1, p.drop_t, thi);
           s[i] = keep ? pv * p.drop_rp : 0.f;                    // P_drop, for dV
           dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + nd[i]);  // dS = P (dP - D)
         } else {
@@ -389,6 +392,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int q0 = qt * BR;
   const int qw = q0 + wave * 32;
   const int myq = qw + l32;
+  [[maybe_unused]] const DropKey dk{(uint32_t)bh, p.drop_offset, p.seed_lo, p.seed_hi};
+  [[maybe_unused]] const uint32_t thi = p.drop_t << 16;
 
   int klim = N;
   if (p.kv_len) klim = min(klim, max(p.kv_len[b], 0));
@@ -478,19 +483,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         dp = mfma32(*reinterpret_cast<const typename T::vec8*>(sV + off), gf[st], dp);
         if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
-      // Dropout words: element i is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8; one Philox
-      // call covers four consecutive keys of this lane's query.
-      uint32_t kwd[DROP ? 16 : 1];
-      if constexpr (DROP) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int key0 = k0 + kb * 32 + 16 * (g >> 1) + 8 * hi + 4 * (g & 1);
-          const u32x4 w = philox4x32_10((uint32_t)key0 >> 2, (uint32_t)myq, (uint32_t)bh,
-                                        p.drop_offset, p.seed_lo, p.seed_hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kwd[8 * (g >> 1) + 4 * (g & 1) + e] = w[e];
-        }
-      }
+      // Dropout draws: element i is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8.
+      uint32_t kwd[DROP ? 8 : 1];
+      if constexpr (DROP) drop_words_query_lane(kwd, k0 + kb * 32 + 8 * hi, myq, dk);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = fast_exp2(s[i] * sc - lq);
@@ -500,7 +495,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           if (!ok) pv = 0.f;
         }
         if constexpr (DROP) {
-          const bool keep = kwd[i] >= p.drop_t;
+          const bool keep = drop_keep(kwd[i >> 1], i & 1, p.drop_t, thi);
           dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + ndq);  // dS = P (dP - D)
         } else {
           dp[i] = pv * (dp[i] + ndq);
@@ -594,7 +589,7 @@ hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {
-  if (p.drop_t != 0)
+  if (p.drop_on)
     return dtype == kF16 ? launch_bwd_t<F16, true>(p, d, stream)
                          : launch_bwd_t<Bf16, true>(p, d, stream);
   return dtype == kF16 ? launch_bwd_t<F16, false>(p, d, stream)

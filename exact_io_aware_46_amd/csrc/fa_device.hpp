@@ -178,22 +178,65 @@ __device__ __forceinline__ i16x4 lds_tr4(const void* lds_ptr) {
 // Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel
 // random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit
 // products, the high halves xored with the other two counter words and the key, the key
-// bumped by a Weyl constant each round. The dropout mask of element (query i, key j) is
-// word j & 3 of the output for counter (j >> 2, i, b*H + h, offset) and key = seed.
+// bumped by a Weyl constant each round. The three-way xors are single v_bitop3 ops.
+//
+// Dropout draws: the call with counter (j >> 2, i >> 1, b*H + h, offset) and key = seed
+// covers queries i, i^1 and keys 4*(j/4) .. +3 of head (b, h): output word j & 3 holds
+// the 16-bit draw of the even query in its low half and of the odd query in its high
+// half. An element is kept iff its draw >= t = floor(p * 2^16).
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);  // a ^ b ^ c
     c1 = (uint32_t)p1;
-    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
   return (u32x4){c0, c1, c2, c3};
+}
+
+struct DropKey {
+  uint32_t bh, offset, seed_lo, seed_hi;
+};
+
+// Keep test of the draw in the low (odd = false) or high (odd = true) half of a word;
+// thi = t << 16.
+__device__ __forceinline__ bool drop_keep(uint32_t word, bool odd, uint32_t t, uint32_t thi) {
+  return odd ? word >= thi : (word & 0xFFFFu) >= t;
+}
+
+// Draws of one 32-key block for a lane that owns one query (forward and dQ kernels).
+// Element i (0..15) of the lane is key kq0 + 16*(i/8) + i%8 (kq0 = block start + 8*hi),
+// i.e. key quad g = i/4 starts at kq0 + 16*(g/2) + 4*(g%2). Lanes l and l^1 own queries
+// 2m and 2m+1 (query parity = lane parity) and the same keys, so they share the block's
+// four calls: the lane of parity par computes quads g = 2*par, 2*par+1, keeps its query's
+// halves and hands the partner the other halves through a DPP exchange. On exit w[h]
+// holds the draw of element 2h in its low half and of element 2h+1 in its high half.
+__device__ __forceinline__ void drop_words_query_lane(uint32_t (&w)[8], int kq0, int query,
+                                                      const DropKey& dk) {
+  const int par = query & 1;
+  const uint32_t sel_mine = par ? 0x07060302u : 0x05040100u;  // high : low halves
+  const uint32_t sel_give = par ? 0x05040100u : 0x07060302u;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int key0 = kq0 + 16 * par + 4 * c;
+    const u32x4 r = philox4x32_10((uint32_t)key0 >> 2, (uint32_t)query >> 1, dk.bh,
+                                  dk.offset, dk.seed_lo, dk.seed_hi);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // v_perm_b32(b, a, sel): bytes 0-3 come from a, 4-7 from b.
+      const uint32_t mine = __builtin_amdgcn_perm(r[2 * h + 1], r[2 * h], sel_mine);
+      const uint32_t give = __builtin_amdgcn_perm(r[2 * h + 1], r[2 * h], sel_give);
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
+      w[2 * c + h] = par ? recv : mine;      // quads 0, 1: computed by the even lane
+      w[4 + 2 * c + h] = par ? mine : recv;  // quads 2, 3: computed by the odd lane
+    }
+  }
 }
 
 // 4x4 transpose of 32-bit values across the 4 lanes of each quad (DPP quad permutes):

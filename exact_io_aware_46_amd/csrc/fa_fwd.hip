@@ -204,19 +204,17 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
       }
     l_run += lsum;  // the normaliser is that of the undropped softmax
     if constexpr (DROP) {
-      // Dropout: element i of block kb is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8; one
-      // Philox call covers four consecutive keys of this lane's query.
+      // Dropout: element i of block kb is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8.
+      const DropKey dk{(uint32_t)bh, p.drop_offset, p.seed_lo, p.seed_hi};
+      const uint32_t thi = p.drop_t << 16;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        uint32_t w[8];
+        drop_words_query_lane(w, k0 + kb * 32 + 8 * hi, myq, dk);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int key0 = k0 + kb * 32 + 16 * (g >> 1) + 8 * hi + 4 * (g & 1);
-          const u32x4 w = philox4x32_10((uint32_t)key0 >> 2, (uint32_t)myq, (uint32_t)bh,
-                                        p.drop_offset, p.seed_lo, p.seed_hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (w[e] < p.drop_t) s[kb][8 * (g >> 1) + 4 * (g & 1) + e] = 0.f;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (!drop_keep(w[i >> 1], i & 1, p.drop_t, thi)) s[kb][i] = 0.f;
+      }
     }
 
     // O^T += V^T P^T. V^T comes from the row-major V tile through transpose loads: lane
@@ -286,7 +284,7 @@ hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int dtype, hipStream_t stream) {
-  if (p.drop_t != 0)
+  if (p.drop_on)
     return dtype == kF16 ? launch_fwd_t<F16, true>(p, d, stream)
                          : launch_fwd_t<Bf16, true>(p, d, stream);
   return dtype == kF16 ? launch_fwd_t<F16, false>(p, d, stream)

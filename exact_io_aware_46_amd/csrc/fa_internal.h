@@ -18,8 +18,10 @@ struct FwdParams {
   float scale;
   int causal;
   int wl, wr;  // sliding window: keys q - wl .. q + wr; negative = no limit on that side
-  // Dropout (used only by the kernels built for it): an element is kept iff its Philox
-  // word is >= drop_t; kept probabilities are scaled by drop_rp = 1 / (1 - p).
+  // Dropout (used only by the kernels built for it, launched iff drop_on): an element is
+  // kept iff its 16-bit Philox draw is >= drop_t = floor(p * 2^16); kept probabilities
+  // are scaled by drop_rp = 1 / (1 - p).
+  int drop_on;
   uint32_t drop_t;
   float drop_rp;
   uint32_t seed_lo, seed_hi, drop_offset;
@@ -43,6 +45,7 @@ struct BwdParams {
   float scale;
   int causal;
   int wl, wr;
+  int drop_on;  // as in FwdParams
   uint32_t drop_t;
   float drop_rp;
   uint32_t seed_lo, seed_hi, drop_offset;

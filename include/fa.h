@@ -146,12 +146,15 @@ int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* 
  * (amentiraz.github.io), section 分块计算整体流程, lists dropout among the fused operations,
  * and the fmread.com report's 算法设计 section says backward recomputes instead of storing.
  * O = (P * keep / (1 - dropout_p)) V, with LSE the statistic of the undropped softmax.
- * keep for element (query i, key j) of head (b, h): word j & 3 of Philox4x32-10 (Salmon et
- * al., SC 2011) with key = seed (low word first) and counter (j >> 2, i, b*H + h, offset);
- * kept iff the word >= floor(dropout_p * 2^32). The backward must get the same dropout_p,
+ * keep for element (query i, key j) of head (b, h): Philox4x32-10 (Salmon et al., SC 2011)
+ * with key = seed (low word first) and counter (j >> 2, i >> 1, b*H + h, offset); output
+ * word j & 3, its low 16 bits for even i and its high 16 bits for odd i, is the element's
+ * draw r, and the element is kept iff r >= floor(dropout_p * 2^16) (dropout_p is resolved
+ * to 2^-16; the scale stays 1 / (1 - dropout_p)). The backward must get the same dropout_p,
  * seed and offset as the forward. dtype: 0 = bfloat16, 1 = fp16 (q, k, v, o, dO, dq, dk, dv
  * in that type). Every mask as in fa_fwd_window. dropout_p = 0 runs the kernels without
- * dropout. Errors: FA_ERR_DROPOUT for dropout_p outside [0, 1) or NaN, FA_ERR_DTYPE for an
+ * dropout; any dropout_p > 0 runs the dropout kernels, even where floor(dropout_p * 2^16)
+ * is 0 (then every element is kept and scaled by 1 / (1 - dropout_p)). Errors: FA_ERR_DROPOUT for dropout_p outside [0, 1) or NaN, FA_ERR_DTYPE for an
  * unknown dtype, otherwise as fa_fwd_window / fa_bwd_window. */
 int fa_fwd_dropout(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, float scale, int causal,
