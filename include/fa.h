@@ -143,8 +143,10 @@ int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* 
 
 /* Dropout on the attention probabilities, fused into the kernels and regenerated in the
  * backward pass (nothing of size N x N is stored): "FlashAttention学习笔记"
- * (amentiraz.github.io), section 分块计算整体流程, lists dropout among the fused operations,
- * and the fmread.com report's 算法设计 section says backward recomputes instead of storing.
+ * (amentiraz.github.io), section Kernel融合, lists dropout among the operations fused into
+ * one kernel, and its section 分块计算整体流程(Tiling) applies it to each block's scores on
+ * the way to P̂; the fmread.com report's 算法设计 section says backward recomputes instead
+ * of storing.
  * O = (P * keep / (1 - dropout_p)) V, with LSE the statistic of the undropped softmax.
  * keep for element (query i, key j) of head (b, h): Philox4x32-10 (Salmon et al., SC 2011)
  * with key = seed (low word first) and counter (j >> 2, i >> 1, b*H + h, offset); output

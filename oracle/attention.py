@@ -36,9 +36,11 @@ notes of the repository):
   key j is allowed for query i iff i - left <= j <= i + right, a negative bound meaning
   no limit on that side (so (-1, 0) is the causal mask);
 * the masks compose by logical AND;
-* dropout, which FlashAttention fuses into the kernel ("FlashAttention学习笔记", section
-  分块计算整体流程: the fused operations; the report's backward bullet: nothing of size
-  N x N is stored, so the dropout mask is regenerated), is read as the usual inverted
+* dropout, which FlashAttention fuses into the kernel ("FlashAttention学习笔记": section
+  Kernel融合 lists it among the operations fused into one kernel, and section
+  分块计算整体流程 applies it, with the mask, to each block's scores on the way to P̂;
+  the report's backward bullet: nothing of size N x N is stored, so the dropout mask is
+  regenerated), is read as the usual inverted
   dropout on the attention probabilities: P_drop = P * keep / (1 - p), O = P_drop V, with
   LSE the statistic of the undropped softmax. keep is drawn from a counter-based
   generator so that backward can regenerate it: Philox4x32-10 (Salmon, Moraes, Dror and
