@@ -275,9 +275,11 @@ def main():
     # Kernel template names as the profiler prints them.
     tn = "fa::F16" if wl.dtype == "f16" else "fa::Bf16"
     dr = "true" if wl.dropout is not None and wl.dropout[0] > 0 else "false"
-    k_dkdv = f"bwd_dkdv_kernel<{tn}, {wl.d}, {dr}>"
-    k_dq = f"bwd_dq_kernel<{tn}, {wl.d}, 64, {dr}>"
-    k_fwd = f"fwd_kernel<{tn}, {wl.d}, 64, {dr}>"
+    kd = 128 if wl.d > 64 else 64                              # kernel head dim
+    pad = "false" if wl.d == kd else "true"                    # zero-padded to kd
+    k_dkdv = f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}>"
+    k_dq = f"bwd_dq_kernel<{tn}, {kd}, 64, {dr}, {pad}>"
+    k_fwd = f"fwd_kernel<{tn}, {kd}, 64, {dr}, {pad}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

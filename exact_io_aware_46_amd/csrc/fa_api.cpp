@@ -22,7 +22,7 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // fit in a signed 32-bit int, and the grid size in a 32-bit unsigned.
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_UNSUPPORTED_D;
   const long long rows = (long long)B * H * N;
   if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
   if ((long long)N * d > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -33,9 +33,9 @@ int check_shape(int B, int H, int N, int d) {
 // side, so it is stored as N (this also keeps every index sum in the kernels in range).
 int clamp_window(int w, int N) { return w < 0 ? -1 : (w > N ? N : w); }
 
-// Dropout parameters: drop an element iff its 32-bit Philox word is below
-// floor(p * 2^32); scale kept probabilities by 1 / (1 - p). p = 0 selects the kernels
-// without dropout.
+// Dropout parameters: drop an element iff its 16-bit Philox draw is below
+// floor(p * 2^16); scale kept probabilities by 1 / (1 - p). p = 0 selects the kernels
+// without dropout, any p > 0 the kernels with it.
 int set_dropout(float p, uint64_t seed, uint32_t offset, int* on, uint32_t* t, float* rp,
                 uint32_t* slo, uint32_t* shi, uint32_t* off) {
   if (!(p >= 0.f && p < 1.f)) return FA_ERR_DROPOUT;
@@ -73,7 +73,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the problem must fit 32-bit indexing)";
-    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: multiples of 8 from 8 to 128)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse/delta 4, workspace 256)";
     case FA_ERR_SCALE: return "scale must be finite and nonzero";
     case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -112,6 +112,7 @@ int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
+  p.dh = d;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
   if ((st = set_dropout(dropout_p, seed, offset, &p.drop_on, &p.drop_t, &p.drop_rp, &p.seed_lo,
@@ -234,6 +235,7 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.B = B; p.H = H; p.N = N;
   p.scale = scale;
   p.causal = causal ? 1 : 0;
+  p.dh = d;
   p.wl = clamp_window(window_left, N);
   p.wr = clamp_window(window_right, N);
   if ((st = set_dropout(dropout_p, seed, offset, &p.drop_on, &p.drop_t, &p.drop_rp, &p.seed_lo,

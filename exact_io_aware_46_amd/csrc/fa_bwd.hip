@@ -41,16 +41,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ delta,
                                                       float* __restrict__ lse2, int rows,
-                                                      float dsign) {
-  constexpr int TPR = D / 8;        // threads per row, 8 elements each
+                                                      int dh, float dsign) {
+  constexpr int TPR = D / 8;        // threads per row, 8 elements each (head dim dh <= D)
   constexpr int RPB = 256 / TPR;    // rows per block
   const int tid = threadIdx.x;
   const long row = (long)blockIdx.x * RPB + tid / TPR;
   const int c = tid % TPR;
   float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = ldg16(o + row * D + c * 8);
-    const u32x4 g = ldg16(dO + row * D + c * 8);
+  if (row < rows && c < (dh >> 3)) {
+    const u32x4 a = ldg16(o + row * dh + c * 8);
+    const u32x4 g = ldg16(dO + row * dh + c * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc += T::lo(a[w]) * T::lo(g[w]);
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // key group sum their dK, dV partials through LDS at the end. Two waves per SIMD let the
 // hardware overlap one wave's exponentials with the other's matrix products. K and V of
 // the tile stay in LDS (row-major, swizzled) for the whole pass.
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool PAD>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
   constexpr int BQ = 64;              // queries per step
@@ -121,7 +121,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   [[maybe_unused]] const DropKey dk{(uint32_t)bh, p.drop_offset, p.seed_lo, p.seed_hi};
   [[maybe_unused]] const uint32_t thi = p.drop_t << 16;
 
-  const size_t hoff = (size_t)bh * N * D;
+  // Row stride and valid 16-byte chunks per row: with PAD the head dim p.dh is below D
+  // and the tiles are zero-padded to D columns.
+  const int ld = PAD ? p.dh : D;
+  const int cha = PAD ? p.dh >> 3 : CH;
+  const size_t hoff = (size_t)bh * N * ld;
   const uint16_t* __restrict__ Q = p.q + hoff;
   const uint16_t* __restrict__ K = p.k + hoff;
   const uint16_t* __restrict__ V = p.v + hoff;
@@ -162,14 +166,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       const int byte = g * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
-      const size_t goff = (size_t)min(q0 + row, N - 1) * D + lch * 8;
-      g2lds16(Q + goff, dQs + g * 1024);
-      g2lds16(dO + goff, ddO + g * 1024);
+      const size_t goff = (size_t)min(q0 + row, N - 1) * ld + lch * 8;
+      if (!PAD || lch < cha) {
+        g2lds16(Q + goff, dQs + g * 1024);
+        g2lds16(dO + goff, ddO + g * 1024);
+      }
     }
     if (wave == 0) g2lds4(L2 + min(q0 + lane, N - 1), dL);
     if (wave == 1) g2lds4(DL + min(q0 + lane, N - 1), dD);
   };
 
+  if constexpr (PAD) {
+    zero_pad<CH>(sQ0, QTILE, cha, tid, 512);
+    zero_pad<CH>(sQ1, QTILE, cha, tid, 512);
+    zero_pad<CH>(sdO0, QTILE, cha, tid, 512);
+    zero_pad<CH>(sdO1, QTILE, cha, tid, 512);
+    zero_pad<CH>(sK, KTILE, cha, tid, 512);
+    zero_pad<CH>(sV, KTILE, cha, tid, 512);
+  }
   int qt = next_q(qt_begin);
   if (qt < qt_end) {
     // K and V of the tile (rows past klim fetch row klim-1; those keys are masked).
@@ -179,9 +193,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       const int byte = g * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
-      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
-      g2lds16(K + goff, sK + g * 1024);
-      g2lds16(V + goff, sV + g * 1024);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * ld + lch * 8;
+      if (!PAD || lch < cha) {
+        g2lds16(K + goff, sK + g * 1024);
+        g2lds16(V + goff, sV + g * 1024);
+      }
     }
     issue_q(qt, sQ0, sdO0, sL0, sD0);
   }
@@ -343,8 +359,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
         const float dk = acc_dk[j][i] + *reinterpret_cast<const float*>(bufk + slot(j, i));
         const float dv = acc_dv[j][i] + *reinterpret_cast<const float*>(bufv + slot(j, i));
-        if (key < N) {
-          const size_t off = hoff + (size_t)key * D + j * 32 + l32;
+        if (key < N && (!PAD || j * 32 + l32 < ld)) {
+          const size_t off = hoff + (size_t)key * ld + j * 32 + l32;
           p.dk[off] = (uint16_t)T::bits(dk * p.scale);
           p.dv[off] = (uint16_t)T::bits(dv);
         }
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <typename T, int D, int BC, bool DROP>
+template <typename T, int D, int BC, bool DROP, bool PAD>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;
@@ -383,7 +399,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int grp = lane >> 4;
   const int t16 = lane & 15;
 
-  const size_t hoff = (size_t)bh * N * D;
+  // Row stride and valid 16-byte chunks per row: with PAD the head dim p.dh is below D
+  // and the tiles are zero-padded to D columns.
+  const int ld = PAD ? p.dh : D;
+  const int cha = PAD ? p.dh >> 3 : CH;
+  const size_t hoff = (size_t)bh * N * ld;
   const uint16_t* __restrict__ Q = p.q + hoff;
   const uint16_t* __restrict__ K = p.k + hoff;
   const uint16_t* __restrict__ V = p.v + hoff;
@@ -423,9 +443,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       const int byte = g * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
-      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
-      g2lds16(K + goff, dK + g * 1024);
-      g2lds16(V + goff, dV + g * 1024);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * ld + lch * 8;
+      if (!PAD || lch < cha) {
+        g2lds16(K + goff, dK + g * 1024);
+        g2lds16(V + goff, dV + g * 1024);
+      }
     }
   };
 
@@ -433,6 +455,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   // exponent: P = exp2(S * scale * log2(e) - LSE * log2(e)).
   const float sc = p.scale * kLog2e;
 
+  if constexpr (PAD) {
+    zero_pad<CH>(sK0, TILE, cha, tid, 512);
+    zero_pad<CH>(sV0, TILE, cha, tid, 512);
+    zero_pad<CH>(sK1, TILE, cha, tid, 512);
+    zero_pad<CH>(sV1, TILE, cha, tid, 512);
+  }
   int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
@@ -442,9 +470,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (myq < N) {
-      x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
-      y = ldg16(dO + (size_t)myq * D + 16 * s + 8 * hi);
+    if (myq < N && (!PAD || 2 * s + hi < cha)) {
+      x = ldg16(Q + (size_t)myq * ld + 16 * s + 8 * hi);
+      y = ldg16(dO + (size_t)myq * ld + 16 * s + 8 * hi);
     }
     qf[s] = as_vec<T>(x);
     gf[s] = as_vec<T>(y);
@@ -533,7 +561,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
   // dQ = scale * dS K.
   if (myq < N) {
-    uint16_t* row = p.dq + hoff + (size_t)myq * D;
+    uint16_t* row = p.dq + hoff + (size_t)myq * ld;
 #pragma unroll
     for (int j = 0; j < DB; ++j)
 #pragma unroll
@@ -541,7 +569,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         u32x2 w;
         w[0] = T::pack(acc[j][4 * g + 0] * p.scale, acc[j][4 * g + 1] * p.scale);
         w[1] = T::pack(acc[j][4 * g + 2] * p.scale, acc[j][4 * g + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g + 4 * hi) = w;
+        if (!PAD || j * 32 + 8 * g + 4 * hi < ld)
+          *reinterpret_cast<u32x2*>(row + j * 32 + 8 * g + 4 * hi) = w;
       }
   }
 }
@@ -551,14 +580,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 template <typename T>
 hipError_t launch_pre_t(const uint16_t* o, const uint16_t* dO, const float* lse, float* delta,
                         float* lse2, int rows, int d, float dsign, hipStream_t stream) {
-  const int rpb = 256 / (d / 8);
+  const int dt = d > 64 ? 128 : 64;  // threads per row cover dt columns
+  const int rpb = 256 / (dt / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  if (d == 128)
+  if (dt == 128)
     hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows, dsign);
+                       lse2, rows, d, dsign);
   else
     hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows, dsign);
+                       lse2, rows, d, dsign);
   return hipGetLastError();
 }
 
@@ -569,6 +599,15 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
                        : launch_pre_t<Bf16>(o, dO, lse, delta, lse2, rows, d, dsign, stream);
 }
 
+template <typename T, int D, bool DROP, bool PAD>
+hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD>), g_kv, dim3(512), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DROP, PAD>), g_q, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   const int rows = p.B * p.H * p.N;
@@ -576,16 +615,12 @@ hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);
-  if (d == 128) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 128, DROP>), g_kv, dim3(512), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 128, 64, DROP>), g_q, dim3(512), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, 64, DROP>), g_kv, dim3(512), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, 64, 64, DROP>), g_q, dim3(512), 0, stream, p);
-  }
-  return hipGetLastError();
+  // d = 64 and 128 run their own kernels; other head dims the next one up, zero-padded.
+  if (d == 128)
+    return launch_main<T, 128, DROP, false>(p, g_kv, g_q, stream);
+  if (d > 64) return launch_main<T, 128, DROP, true>(p, g_kv, g_q, stream);
+  if (d == 64) return launch_main<T, 64, DROP, false>(p, g_kv, g_q, stream);
+  return launch_main<T, 64, DROP, true>(p, g_kv, g_q, stream);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {

@@ -142,6 +142,20 @@ __device__ __forceinline__ int swz_off(int row, int col) {
   return row * (CH * 16) + (((col >> 3) ^ swz<CH>(row)) << 4) + ((col & 7) << 1);
 }
 
+// Zeroes the padding of a swizzled tile of `bytes` bytes (CH chunks of 16 bytes per row)
+// that holds rows of a head dim below the tile's: every chunk whose logical column chunk
+// (physical chunk XOR the row's swizzle) is >= `valid`. The tile copies never write these
+// chunks, so they stay zero for the whole kernel. Run by all `nthreads` threads.
+template <int CH>
+__device__ __forceinline__ void zero_pad(char* tile, int bytes, int valid, int tid,
+                                         int nthreads) {
+  for (int c = tid; c < bytes / 16; c += nthreads) {
+    const int row = c / CH;
+    if (((c % CH) ^ swz<CH>(row)) >= valid)
+      *reinterpret_cast<u32x4*>(tile + 16 * c) = (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // lds_base + 16 * l (lds_base must be the same for the whole wave).
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {

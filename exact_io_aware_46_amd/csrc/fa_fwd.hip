@@ -30,7 +30,7 @@
 namespace fa {
 namespace {
 
-template <typename T, int D, int BC, bool DROP>
+template <typename T, int D, int BC, bool DROP, bool PAD>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
   constexpr int NS = D / 16;        // contraction steps of the score MFMA
@@ -64,7 +64,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   const int grp = lane >> 4;  // 16-lane group (transpose loads)
   const int t16 = lane & 15;
 
-  const size_t hoff = (size_t)bh * N * D;
+  // Row stride and valid 16-byte chunks per row: with PAD the head dim p.dh is below D
+  // and the tiles are zero-padded to D columns.
+  const int ld = PAD ? p.dh : D;
+  const int cha = PAD ? p.dh >> 3 : CH;
+  const size_t hoff = (size_t)bh * N * ld;
   const uint16_t* __restrict__ Q = p.q + hoff;
   const uint16_t* __restrict__ K = p.k + hoff;
   const uint16_t* __restrict__ V = p.v + hoff;
@@ -105,9 +109,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
       const int byte = g * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
-      const size_t goff = (size_t)min(k0 + row, klim - 1) * D + lch * 8;
-      g2lds16(K + goff, dK + g * 1024);
-      g2lds16(V + goff, dV + g * 1024);
+      const size_t goff = (size_t)min(k0 + row, klim - 1) * ld + lch * 8;
+      if (!PAD || lch < cha) {
+        g2lds16(K + goff, dK + g * 1024);
+        g2lds16(V + goff, dV + g * 1024);
+      }
     }
   };
 
@@ -116,6 +122,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   const float sc = fabsf(p.scale) * kLog2e;
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
 
+  if constexpr (PAD) {
+    zero_pad<CH>(sK0, TILE, cha, tid, 512);
+    zero_pad<CH>(sV0, TILE, cha, tid, 512);
+    zero_pad<CH>(sK1, TILE, cha, tid, 512);
+    zero_pad<CH>(sV1, TILE, cha, tid, 512);
+  }
   int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (myq < N) x = ldg16(Q + (size_t)myq * D + 16 * s + 8 * hi);
+    if (myq < N && (!PAD || 2 * s + hi < cha)) x = ldg16(Q + (size_t)myq * ld + 16 * s + 8 * hi);
     x[0] ^= qsign; x[1] ^= qsign; x[2] ^= qsign; x[3] ^= qsign;
     qf[s] = as_vec<T>(x);
   }
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   if (myq < N) {
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if constexpr (DROP) inv *= p.drop_rp;  // kept probabilities are scaled by 1 / (1 - p)
-    uint16_t* orow = p.o + hoff + (size_t)myq * D;
+    uint16_t* orow = p.o + hoff + (size_t)myq * ld;
 #pragma unroll
     for (int j = 0; j < DB; ++j)
 #pragma unroll
@@ -263,7 +275,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
         u32x2 w;
         w[0] = T::pack(acc[j][4 * g + 0] * inv, acc[j][4 * g + 1] * inv);
         w[1] = T::pack(acc[j][4 * g + 2] * inv, acc[j][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + j * 32 + 8 * g + 4 * hi) = w;
+        if (!PAD || j * 32 + 8 * g + 4 * hi < ld)
+          *reinterpret_cast<u32x2*>(orow + j * 32 + 8 * g + 4 * hi) = w;
       }
     if (hi == 0)
       p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -kInf;
@@ -276,10 +289,15 @@ template <typename T, bool DROP>
 hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
   const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
+  // d = 64 and 128 run their own kernels; other head dims the next one up, zero-padded.
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false>), grid, dim3(512), 0, stream, p);
+  else if (d > 64)
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true>), grid, dim3(512), 0, stream, p);
+  else if (d == 64)
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ struct FwdParams {
   int B, H, N;
   float scale;
   int causal;
+  int dh;      // head dim: a multiple of 8 up to 128; the kernels are built for D = 64
+               // and 128 and run a smaller dh on tiles zero-padded to D columns
   int wl, wr;  // sliding window: keys q - wl .. q + wr; negative = no limit on that side
   // Dropout (used only by the kernels built for it, launched iff drop_on): an element is
   // kept iff its 16-bit Philox draw is >= drop_t = floor(p * 2^16); kept probabilities
@@ -44,6 +46,7 @@ struct BwdParams {
   int B, H, N;
   float scale;
   int causal;
+  int dh;      // as in FwdParams
   int wl, wr;
   int drop_on;  // as in FwdParams
   uint32_t drop_t;

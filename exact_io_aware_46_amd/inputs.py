@@ -76,8 +76,8 @@ class Workload:
 
 # The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
 # BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, the long
-# head set with a sliding window, the long causal head set in fp16, and the long causal
-# head set with attention dropout.
+# head set with a sliding window, the long causal head set in fp16, the long causal head
+# set with attention dropout, and the long causal head set at head dims 96 and 32.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -98,6 +98,12 @@ WORKLOADS = {
     "long_causal_16k_dropout": Workload("long_causal_16k_dropout", 1, 16, 16384, 128,
                                         causal=True, seed=46008,
                                         dropout=(0.1, 0x5EED_0000_B3D8, 0)),
+    # The long causal head set at head dims 96 and 32, which run the 128 and 64 kernels on
+    # zero-padded tiles.
+    "long_causal_16k_d96": Workload("long_causal_16k_d96", 1, 16, 16384, 96, causal=True,
+                                    seed=46009),
+    "long_causal_16k_d32": Workload("long_causal_16k_d32", 1, 16, 16384, 32, causal=True,
+                                    seed=46010),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

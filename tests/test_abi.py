@@ -75,7 +75,8 @@ def test_fwd_bad_shape(lib, B, H, N):
     assert fwd(lib, B=B, H=H, N=N) == 2
 
 
-@pytest.mark.parametrize("d", [0, 32, 96, 256, -64])
+# Supported: multiples of 8 from 8 to 128.
+@pytest.mark.parametrize("d", [0, 4, 20, 100, 136, 256, -64])
 def test_fwd_unsupported_head_dim(lib, d):
     assert fwd(lib, d=d) == 3
 
@@ -110,7 +111,7 @@ def test_bwd_errors(lib):
     for i in range(10):
         assert bwd(lib, {i: 0}) == 1
     assert bwd(lib, B=0) == 2
-    assert bwd(lib, d=80) == 3
+    assert bwd(lib, d=136) == 3
     assert bwd(lib, {0: A + 8}) == 4
     assert bwd(lib, ws_off=16) == 4                  # workspace needs 256-byte alignment
     assert bwd(lib, scale=float("nan")) == 5
@@ -121,7 +122,7 @@ def test_bwd_errors(lib):
 
 def test_preprocess_errors(lib):
     assert lib.fa_bwd_preprocess(None, A, A + T_BYTES, 1, 1, 8, 64, None) == 1
-    assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 2 * T_BYTES, 1, 1, 8, 48, None) == 3
+    assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 2 * T_BYTES, 1, 1, 8, 44, None) == 3
     assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 2, 1, 1, 8, 64, None) == 4
     assert lib.fa_bwd_preprocess(A, A + T_BYTES, A + 4, 1, 1, 8, 64, None) == 7
 
@@ -147,7 +148,7 @@ def test_window_entry_points_validate_like_the_others(lib):
     fwd_args = lambda q, d, scale: (q, p[1], p[2], p[3], p[4], 1, 1, 64, d, scale, 0, None,
                                     None, 3, -1, None)
     assert lib.fa_fwd_window(*fwd_args(None, 64, 0.125)) == 1          # FA_ERR_NULL
-    assert lib.fa_fwd_window(*fwd_args(p[0], 96, 0.125)) == 3          # FA_ERR_UNSUPPORTED_D
+    assert lib.fa_fwd_window(*fwd_args(p[0], 200, 0.125)) == 3         # FA_ERR_UNSUPPORTED_D
     assert lib.fa_fwd_window(*fwd_args(p[0], 64, float("nan"))) == 5   # FA_ERR_SCALE
     assert lib.fa_fwd_window(*fwd_args(p[0] + 2, 64, 0.125)) == 4     # FA_ERR_ALIGN
     ws = A + 64 * T_BYTES
@@ -165,7 +166,7 @@ def test_f16_entry_points_validate_like_the_others(lib):
     p = ptrs(9)
     assert lib.fa_fwd_f16(None, p[1], p[2], p[3], p[4], 1, 1, 64, 64, 0.125, 0, None, None,
                           -1, -1, None) == 1                           # FA_ERR_NULL
-    assert lib.fa_fwd_f16(p[0], p[1], p[2], p[3], p[4], 1, 1, 64, 32, 0.125, 0, None, None,
+    assert lib.fa_fwd_f16(p[0], p[1], p[2], p[3], p[4], 1, 1, 64, 12, 0.125, 0, None, None,
                           -1, -1, None) == 3                           # FA_ERR_UNSUPPORTED_D
     assert lib.fa_bwd_preprocess_f16(p[0], p[1], p[2] + 1, 1, 1, 64, 64, None) == 4  # ALIGN
     ws = A + 64 * T_BYTES

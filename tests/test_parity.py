@@ -13,7 +13,7 @@ import torch
 
 from exact_io_aware_46_amd import inputs as inp
 from oracle import attention as orc
-from tests.gpu_util import Run, check_all, check_grad, check_lse, check_o, say, to_f64
+from tests.gpu_util import Run, check_all, check_grad, check_lse, check_o, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -233,31 +233,34 @@ def test_workload_full_compare(name):
 
 
 @pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k", "sliding_window_16k",
-                                  "long_causal_16k_f16"])
+                                  "long_causal_16k_f16", "long_causal_16k_dropout",
+                                  "long_causal_16k_d96", "long_causal_16k_d32"])
 def test_workload_sampled_compare(name):
     wl = inp.WORKLOADS[name]
     x = inp.make_inputs(wl)
     say(f"[parity] {name} (sampled rows + one full head)")
+    slack = 0.0 if wl.dropout is None else DROP_O_SLACK
     res = Run(x.q, x.k, x.v, x.do, wl.scale, wl.causal, x.blockmask, x.kv_len,
-              window=wl.window).result()
+              window=wl.window, dropout=wl.dropout).result()
     for key in res:
         assert np.isfinite(res[key]).all(), key
     sel = _sample_rows(wl, 48, wl.seed)
     o_ref, l_ref = orc.forward_rows(x.q, x.k, x.v, wl.scale, sel, wl.causal, x.blockmask,
-                                    x.kv_len, window=wl.window)
+                                    x.kv_len, window=wl.window, dropout=wl.dropout)
     dq_ref = orc.dq_rows(x.q, x.k, x.v, x.do, wl.scale, sel, wl.causal, x.blockmask, x.kv_len,
-                         window=wl.window)
+                         window=wl.window, dropout=wl.dropout)
     idx = tuple(np.array(sel).T)
-    check_o(res["O"][idx], o_ref, name)
+    check_o(res["O"][idx], o_ref, name, slack)
     check_lse(res["LSE"][idx], l_ref, name)
     check_grad(res["dQ"][idx], dq_ref, "dQ", name)
     b, h = wl.B - 1, wl.H // 2
     say(f"[parity] {name} full head ({b},{h}) oracle")
     kv_b = None if x.kv_len is None else int(x.kv_len[b])
+    drop = None if wl.dropout is None else (*wl.dropout, b * wl.H + h)
     ref = orc.head_backward(orc.as_f64(x.q[b, h]), orc.as_f64(x.k[b, h]),
                             orc.as_f64(x.v[b, h]), orc.as_f64(x.do[b, h]), wl.scale,
-                            wl.causal, x.blockmask, kv_b, window=wl.window)
-    check_o(res["O"][b, h], ref["O"], name)
+                            wl.causal, x.blockmask, kv_b, window=wl.window, dropout=drop)
+    check_o(res["O"][b, h], ref["O"], name, slack)
     check_lse(res["LSE"][b, h], ref["LSE"], name)
     for g in ("dQ", "dK", "dV"):
         check_grad(res[g][b, h], ref[g], g, name)
@@ -488,3 +491,78 @@ def test_dropout_p0_is_bitwise_no_dropout_and_outputs_deterministic(d):
     assert not _bits_equal(a.o, c.o) and not _bits_equal(a.o, e.o)
     with pytest.raises(fa.FAError):
         Run(q, k, v, do, 0.125, True, dropout=(1.0, 1, 0), backward=False)
+
+
+# ------------------------------------------------- head dims other than 64 and 128
+
+@pytest.mark.parametrize("d", [8, 32, 40, 96, 120])
+@pytest.mark.parametrize("N,causal,window,kv,bm", [
+    (1, False, None, None, None),
+    (129, True, None, None, None),
+    (300, False, (60, 20), None, None),
+    (384, True, None, [384, 150], [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
+])
+def test_other_head_dims(d, N, causal, window, kv, bm):
+    B = 1 if kv is None else len(kv)
+    q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=107 + N + d)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    bmn = None if bm is None else np.array(bm, dtype=np.uint8)
+    run_and_check(q, k, v, do, float(np.float32(d ** -0.5)), causal, bmn, kvn,
+                  what=f"head dim {d}", window=window)
+
+
+@pytest.mark.parametrize("d", [24, 96])
+def test_other_head_dims_f16_and_dropout(d):
+    N = 257
+    q, k, v, do = inp.custom_inputs(2, 2, N, d, seed=109 + d, dtype="f16")
+    kv = np.array([257, 100], dtype=np.int32)
+    drop = (0.2, 4242 + d, 1)
+    say(f"[parity] head dim {d} f16 + dropout")
+    res = Run(q, k, v, do, 0.1, True, None, kv, dropout=drop).result()
+    ref = orc.backward(q, k, v, do, 0.1, True, None, kv, dropout=drop)
+    check_all(res, ref, f"head dim {d} f16 dropout", o_rel_slack=DROP_O_SLACK)
+
+
+def _zero_pad_cols(x, dfull):
+    out = np.zeros(x.shape[:-1] + (dfull,), dtype=x.dtype)
+    out[..., :x.shape[-1]] = x
+    return out
+
+
+@pytest.mark.parametrize("d,dfull", [(96, 128), (40, 64)])
+def test_padded_head_dim_is_bitwise_the_full_kernel_on_zero_padded_tensors(d, dfull):
+    """A head dim below 64 / 128 runs the 64 / 128 kernel on tiles zero-padded in LDS and
+    registers; the result must equal, bit for bit, that kernel run on tensors zero-padded
+    in memory (same arithmetic, same order, the extra columns adding exact zeros)."""
+    N = 300
+    q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=113 + d)
+    say(f"[bitexact] head dim {d} vs {dfull} zero-padded")
+    a = Run(q, k, v, do, 0.11, True)
+    b = Run(*(_zero_pad_cols(x, dfull) for x in (q, k, v, do)), 0.11, True)
+    assert _bits_equal(a.lse, b.lse)
+    for name in ("o", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)[..., :d].contiguous()), name
+        assert (to_f64(getattr(b, name))[..., d:] == 0).all(), name
+
+
+@pytest.mark.parametrize("d", [40, 96])
+def test_padded_head_dim_writes_nothing_past_its_outputs(d):
+    """Outputs sit at the start of larger buffers filled with a sentinel; the padded
+    columns are never stored, so everything after each output must keep the sentinel."""
+    import exact_io_aware_46_amd as fa
+    B, H, N = 1, 2, 200
+    q, k, v, do = (to_dev(x) for x in inp.custom_inputs(B, H, N, d, seed=127 + d))
+    n = B * H * N * d
+    guard = 4096
+    bufs = {name: torch.full((n + guard,), 0x5A5A, dtype=torch.int16, device="cuda")
+            for name in ("o", "dq", "dk", "dv")}
+    view = {name: b[:n].view(torch.bfloat16).view(B, H, N, d) for name, b in bufs.items()}
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    say(f"[guard] head dim {d}")
+    fa.fa_fwd_window(q, k, v, view["o"], lse, B, H, N, d, 0.125, 1, None, None, -1, -1)
+    fa.fa_bwd_window(q, k, v, view["o"], lse, do, view["dq"], view["dk"], view["dv"], B, H, N,
+                     d, 0.125, 1, None, None, -1, -1, ws)
+    torch.cuda.synchronize()
+    for name, b in bufs.items():
+        assert (b[n:] == 0x5A5A).all().item(), f"{name} written past its end"
