@@ -75,12 +75,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // key group sum their dK, dV partials through LDS at the end. Two waves per SIMD let the
 // hardware overlap one wave's exponentials with the other's matrix products. K and V of
 // the tile stay in LDS (row-major, swizzled) for the whole pass.
-template <typename T, int D, bool DROP, bool PAD>
+// D, DC, PAD as in the forward: LDS layout head dim, computed head dim, and whether the
+// head dim p.dh is below D.
+template <typename T, int D, bool DROP, bool PAD, int DC>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
   constexpr int BQ = 64;              // queries per step
-  constexpr int NS = D / 16;          // contraction steps over d
-  constexpr int DB = D / 32;          // 32-wide column blocks over d
+  constexpr int NS = DC / 16;         // contraction steps over d
+  constexpr int DB = DC / 32;         // 32-wide column blocks over d
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;
   constexpr int QTILE = BQ * ROWB;    // bytes of one Q (or dO) tile
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     if (wave == 1) g2lds4(DL + min(q0 + lane, N - 1), dD);
   };
 
-  if constexpr (PAD) {
+  if constexpr (PAD && DC == D) {  // padded columns are read: they must hold zeros
     zero_pad<CH>(sQ0, QTILE, cha, tid, 512);
     zero_pad<CH>(sQ1, QTILE, cha, tid, 512);
     zero_pad<CH>(sdO0, QTILE, cha, tid, 512);
@@ -370,12 +372,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <typename T, int D, int BC, bool DROP, bool PAD>
+template <typename T, int D, int BC, bool DROP, bool PAD, int DC>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
-  constexpr int NS = D / 16;
+  constexpr int NS = DC / 16;
   constexpr int KB = BC / 32;
-  constexpr int DB = D / 32;
+  constexpr int DB = DC / 32;
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   // exponent: P = exp2(S * scale * log2(e) - LSE * log2(e)).
   const float sc = p.scale * kLog2e;
 
-  if constexpr (PAD) {
+  if constexpr (PAD && DC == D) {  // padded columns are read: they must hold zeros
     zero_pad<CH>(sK0, TILE, cha, tid, 512);
     zero_pad<CH>(sV0, TILE, cha, tid, 512);
     zero_pad<CH>(sK1, TILE, cha, tid, 512);
@@ -599,12 +601,12 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
                        : launch_pre_t<Bf16>(o, dO, lse, delta, lse2, rows, d, dsign, stream);
 }
 
-template <typename T, int D, bool DROP, bool PAD>
+template <typename T, int D, bool DROP, bool PAD, int DC>
 hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD>), g_kv, dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC>), g_kv, dim3(512), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DROP, PAD>), g_q, dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DROP, PAD, DC>), g_q, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -615,12 +617,14 @@ hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh), g_q((unsigned)((p.N + 255) / 256) * bh);
-  // d = 64 and 128 run their own kernels; other head dims the next one up, zero-padded.
-  if (d == 128)
-    return launch_main<T, 128, DROP, false>(p, g_kv, g_q, stream);
-  if (d > 64) return launch_main<T, 128, DROP, true>(p, g_kv, g_q, stream);
-  if (d == 64) return launch_main<T, 64, DROP, false>(p, g_kv, g_q, stream);
-  return launch_main<T, 64, DROP, true>(p, g_kv, g_q, stream);
+  // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
+  // head dims run the next kernel up on zero-padded tiles.
+  if (d == 128) return launch_main<T, 128, DROP, false, 128>(p, g_kv, g_q, stream);
+  if (d == 96) return launch_main<T, 128, DROP, true, 96>(p, g_kv, g_q, stream);
+  if (d > 64) return launch_main<T, 128, DROP, true, 128>(p, g_kv, g_q, stream);
+  if (d == 64) return launch_main<T, 64, DROP, false, 64>(p, g_kv, g_q, stream);
+  if (d == 32) return launch_main<T, 64, DROP, true, 32>(p, g_kv, g_q, stream);
+  return launch_main<T, 64, DROP, true, 64>(p, g_kv, g_q, stream);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {

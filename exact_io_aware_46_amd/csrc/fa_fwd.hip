@@ -30,12 +30,16 @@
 namespace fa {
 namespace {
 
-template <typename T, int D, int BC, bool DROP, bool PAD>
+// D: head dim of the LDS tile layout (64 or 128). DC: head dim computed on (D, or 32 / 96
+// on the 64 / 128 layout: the contraction and the O columns stop at DC, so the unused
+// chunks of each row are never read). PAD: the head dim p.dh is below D (global rows are
+// p.dh wide; the copies skip chunks at or past it).
+template <typename T, int D, int BC, bool DROP, bool PAD, int DC>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
-  constexpr int NS = D / 16;        // contraction steps of the score MFMA
+  constexpr int NS = DC / 16;       // contraction steps of the score MFMA
   constexpr int KB = BC / 32;       // 32-key blocks per key tile
-  constexpr int DB = D / 32;        // 32-wide column blocks of O
+  constexpr int DB = DC / 32;       // 32-wide column blocks of O
   constexpr int CH = D / 8;         // 16-byte chunks per row
   constexpr int ROWB = D * 2;       // bytes per row
   constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   const float sc = fabsf(p.scale) * kLog2e;
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
 
-  if constexpr (PAD) {
+  if constexpr (PAD && DC == D) {  // padded columns are read: they must hold zeros
     zero_pad<CH>(sK0, TILE, cha, tid, 512);
     zero_pad<CH>(sV0, TILE, cha, tid, 512);
     zero_pad<CH>(sK1, TILE, cha, tid, 512);
@@ -289,15 +293,20 @@ template <typename T, bool DROP>
 hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
   const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
-  // d = 64 and 128 run their own kernels; other head dims the next one up, zero-padded.
+  // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
+  // head dims run the next kernel up on zero-padded tiles.
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false, 128>), grid, dim3(512), 0, stream, p);
+  else if (d == 96)
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 96>), grid, dim3(512), 0, stream, p);
   else if (d > 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 128>), grid, dim3(512), 0, stream, p);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64>), grid, dim3(512), 0, stream, p);
+  else if (d == 32)
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 32>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 64>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -529,11 +529,13 @@ def _zero_pad_cols(x, dfull):
     return out
 
 
-@pytest.mark.parametrize("d,dfull", [(96, 128), (40, 64)])
+@pytest.mark.parametrize("d,dfull", [(96, 128), (40, 64), (32, 64), (72, 128)])
 def test_padded_head_dim_is_bitwise_the_full_kernel_on_zero_padded_tensors(d, dfull):
-    """A head dim below 64 / 128 runs the 64 / 128 kernel on tiles zero-padded in LDS and
-    registers; the result must equal, bit for bit, that kernel run on tensors zero-padded
-    in memory (same arithmetic, same order, the extra columns adding exact zeros)."""
+    """A head dim below 64 / 128 runs on the 64 / 128 layout: 32 and 96 stop the
+    contraction at their width, other dims compute over tiles zero-padded in LDS and
+    registers. Either way the result must equal, bit for bit, the full kernel run on
+    tensors zero-padded in memory (same arithmetic, same order, the extra columns only
+    adding exact zeros)."""
     N = 300
     q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=113 + d)
     say(f"[bitexact] head dim {d} vs {dfull} zero-padded")
