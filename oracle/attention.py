@@ -53,6 +53,21 @@ notes of the repository):
   fixed mask:
   dV = P_drop^T dO, dP = (dO V^T) * keep / (1 - p), D = rowsum(dO * O),
   dS = P * (dP - D);
+* FP8 forward. The deployment page says FlashAttention-3 brought FP8 to the forward pass
+  on H100 ("IO感知计算如何重塑Transformer内存优化技术格局", section 技术演进时间线) and gives
+  no quantisation policy. It is read as follows.
+  - Q, K and V arrive as OCP E4M3 codes (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits; subnormals; the all-ones magnitude is NaN; largest finite 448),
+    with one float32 descale per tensor: q = descale_q * decode(Q8), likewise k and v.
+  - S = scale * q k^T in exact arithmetic, masked as above.
+  - In log2 units t = S * log2(e). With m = ceil(max_j t_j) over the row's allowed keys,
+    P_j = 2^(t_j - m) lies in (0, 1].
+  - P_j is rounded to E4M3, nearest with ties to even, subnormals included, giving Pq_j.
+    l = sum_j P_j is left unrounded.
+  - O = descale_v * sum_j Pq_j decode(V8_j) / l, and LSE = ln sum_j exp(S_j).
+  - The reference m is an integer power of two, so a kernel whose running reference is any
+    integer (in log2 units) quantises the same P, scaled by a power of two. That scaling
+    commutes with the rounding wherever both sides are in the normal range.
 * a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
 * backward is the derivative of the scalar L = sum(dO * O) with respect to Q, K, V:
   dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic, dS = P * (dP - D),
@@ -326,6 +341,106 @@ def dq_rows(q, k, v, do, scale, sel, causal=False, blockmask=None, kv_len=None,
         dS = P * (dP - D[:, None])
         out[n] = (s * (dS @ Kh))[0]
     return out
+
+
+# --------------------------------------------------------------------- FP8 forward
+
+def _e4m3_table() -> np.ndarray:
+    """Value of every E4M3 code 0..255 (OCP: bias 7, subnormals, S.1111.111 = NaN)."""
+    vals = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * m * 2.0 ** -9          # subnormal: m/8 * 2^-6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3 = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 E4M3 codes -> exact float64 values."""
+    return E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round float64 values with |x| <= 448 to the nearest E4M3 value, ties to the even
+    code (the one whose mantissa's last bit is 0). The grid has spacing 2^-9 below 2^-6
+    (subnormals) and 2^(e-3) in binade [2^e, 2^(e+1))."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    assert (a <= E4M3_MAX).all(), "outside the finite E4M3 range"
+    # spacing of the grid at a: 2^-9 for a < 2^-6, else 2^(floor(log2 a) - 3)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    q = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.maximum(e, -6) - 3))
+    n = a / q                      # exact: q is a power of two
+    f = np.floor(n)
+    r = n - f
+    up = (r > 0.5) | ((r == 0.5) & (np.mod(f, 2) == 1))
+    return np.sign(x) * (f + up) * q
+
+
+def head_forward_fp8(Q8, K8, V8, descale, scale, causal=False, blockmask=None,
+                     kv_len_b=None, rows=None, panel=DEFAULT_PANEL, window=None):
+    """One head of the FP8 forward: Q8, K8, V8 are uint8 E4M3 codes [N][d], descale is
+    (descale_q, descale_k, descale_v) (float32 values). Returns (O[rows], LSE[rows])."""
+    dq_, dk_, dv_ = (float(np.float32(x)) for x in descale)
+    Qh, Kh = dq_ * e4m3_decode(Q8), dk_ * e4m3_decode(K8)
+    Vh = e4m3_decode(V8)
+    N = Kh.shape[0]
+    s = _scale64(scale)
+    rows = np.arange(Qh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.zeros((rows.size, Vh.shape[1]))
+    LSE = np.zeros(rows.size)
+    for r0 in range(0, rows.size, panel):
+        rr = rows[r0:r0 + panel]
+        S = _scores(Qh[rr], Kh, s, allowed(rr, N, causal, blockmask, kv_len_b, window))
+        lse = _logsumexp_rows(S)
+        live = np.isfinite(lse)
+        t = S * (1.0 / np.log(2.0))
+        with np.errstate(invalid="ignore"):
+            m = np.ceil(np.where(live, np.max(np.where(np.isfinite(t), t, -np.inf), axis=1), 0))
+        P = np.where(np.isfinite(t), np.exp2(t - m[:, None]), 0.0)
+        l = P.sum(axis=1)
+        Pq = e4m3_round(P)
+        num = Pq @ Vh
+        O[r0:r0 + rr.size] = np.where(live[:, None], dv_ * num / np.where(live, l, 1.0)[:, None], 0.0)
+        LSE[r0:r0 + rr.size] = lse
+    return O, LSE
+
+
+def forward_fp8(q8, k8, v8, descale, scale, causal=False, blockmask=None, kv_len=None,
+                window=None):
+    """All heads of the FP8 forward. q8, k8, v8: uint8 E4M3 codes [B][H][N][d]."""
+    B, H, N, d = q8.shape
+    O = np.zeros((B, H, N, d))
+    LSE = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], LSE[b, h] = head_forward_fp8(q8[b, h], k8[b, h], v8[b, h], descale, scale,
+                                                  causal, blockmask, _kv_len_b(kv_len, b),
+                                                  window=window)
+    return O, LSE
+
+
+def forward_fp8_rows(q8, k8, v8, descale, scale, sel, causal=False, blockmask=None,
+                     kv_len=None, window=None):
+    """Sampled rows of the FP8 forward: ``sel`` is a sequence of (b, h, i)."""
+    d = q8.shape[3]
+    O = np.zeros((len(sel), d))
+    LSE = np.zeros(len(sel))
+    for n, (b, h, i) in enumerate(sel):
+        o, l = head_forward_fp8(q8[b, h], k8[b, h], v8[b, h], descale, scale, causal,
+                                blockmask, _kv_len_b(kv_len, b), rows=[i], window=window)
+        O[n], LSE[n] = o[0], l[0]
+    return O, LSE
 
 
 def delta(o, do):

@@ -17,6 +17,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import attention as orc
 
@@ -647,3 +648,122 @@ def test_dropout_delta_two_ways():
     P /= P.sum(1, keepdims=True)
     Pd = P * orc.dropout_keep(np.arange(N), N, 0, 0.5, 7, 0) * 2.0
     np.testing.assert_allclose(r["D"], (Pd * (do @ v.T)).sum(1), atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 forward
+# Reading: Q, K, V as OCP E4M3 codes with per-tensor descales; P = 2^(t - ceil(max t)) is
+# rounded to E4M3 (nearest, ties to even) before P V; l and LSE use the unrounded P.
+
+def test_e4m3_decode_matches_torch_and_known_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = orc.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x3C: 1.5, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in known.items():
+        assert orc.e4m3_decode(np.uint8(c)) == v
+    assert np.isnan(orc.e4m3_decode(np.uint8(0x7F))) and np.isnan(orc.e4m3_decode(np.uint8(0xFF)))
+
+
+def test_e4m3_round_matches_torch_nearest_even():
+    rng = np.random.Generator(np.random.PCG64(131))
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(20000) * 2.0 ** rng.integers(-14, 8, 20000),
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    grid = orc.E4M3[:127]                                  # 0 .. 448
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)  # exact ties, representable
+    x = np.concatenate([x, mids, -mids, grid.astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(orc.e4m3_round(x.astype(np.float64)), ref)
+    # hand-worked ties: 1 + 1/16 -> 1 (even), 1 + 3/16 -> 1.25, 2^-10 -> 0, 3 * 2^-10 -> 2^-8
+    assert list(orc.e4m3_round(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10]))) == \
+        [1.0, 1.25, 0.0, 2.0 ** -8]
+
+
+def _fp8_codes(shape, seed, sd=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = (sd * rng.standard_normal(shape)).astype(np.float32)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_forward_matches_brute_force():
+    N, d = 13, 8
+    q8, k8, v8 = _fp8_codes((N, d), 133), _fp8_codes((N, d), 134), _fp8_codes((N, d), 135)
+    desc = (0.75, 1.25, 0.5)
+    s = float(np.float32(0.6))
+    O, L = orc.head_forward_fp8(q8, k8, v8, desc, 0.6, causal=True)
+    dec = lambda c: float(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn).double())
+    for i in range(N):
+        sc = [s * math.fsum(0.75 * dec(q8[i, c]) * 1.25 * dec(k8[j, c]) for c in range(d))
+              for j in range(i + 1)]
+        t = [x / math.log(2.0) for x in sc]
+        m = math.ceil(max(t))
+        P = [2.0 ** (x - m) for x in t]
+        Pq = [float(torch.tensor([p], dtype=torch.float32).to(torch.float8_e4m3fn).double())
+              for p in P]
+        l = math.fsum(P)
+        assert abs(L[i] - (m * math.log(2.0) + math.log(l))) < 1e-12
+        for c in range(d):
+            want = 0.5 * math.fsum(Pq[j] * dec(v8[j, c]) for j in range(i + 1)) / l
+            assert abs(O[i, c] - want) < 1e-12, (i, c)
+
+
+def test_fp8_forward_equal_scores_closed_form():
+    # Identical keys: every P_j = p0 = 2^(t0 - ceil t0), so O = descale_v * (Pq0 / p0) * mean(V).
+    N, d = 40, 16
+    q8 = _fp8_codes((N, d), 137)
+    k8 = np.repeat(_fp8_codes((1, d), 138), N, axis=0)
+    v8 = _fp8_codes((N, d), 139)
+    desc = (1.0, 0.5, 2.0)
+    O, L = orc.head_forward_fp8(q8, k8, v8, desc, 0.3)
+    Q, K = orc.e4m3_decode(q8), 0.5 * orc.e4m3_decode(k8)
+    t0 = float(np.float32(0.3)) * (Q @ K[0]) / math.log(2.0)
+    p0 = 2.0 ** (t0 - np.ceil(t0))
+    ratio = orc.e4m3_round(p0) / p0
+    want = 2.0 * ratio[:, None] * orc.e4m3_decode(v8).mean(axis=0)[None, :]
+    np.testing.assert_allclose(O, want, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L, float(np.float32(0.3)) * (Q @ K[0]) + math.log(N), atol=1e-12)
+
+
+def test_fp8_forward_is_plain_attention_within_the_rounding_of_p():
+    # |O_fp8 - O| <= descale_v * (2^-4 sum_j P_j |V_j| + 2^-10 sum_j |V_j|) / l, from
+    # |Pq - P| <= max(2^-4 P, 2^-10); LSE is unchanged.
+    N, d = 200, 32
+    q8, k8, v8 = (_fp8_codes((1, 2, N, d), s) for s in (141, 142, 143))
+    desc = (0.9, 1.1, 0.7)
+    O, L = orc.forward_fp8(q8, k8, v8, desc, 0.2, causal=True)
+    q, k = desc[0] * orc.e4m3_decode(q8), desc[1] * orc.e4m3_decode(k8)
+    v = orc.e4m3_decode(v8)
+    O0, L0 = orc.forward(q, k, desc[2] * v, 0.2, causal=True)
+    np.testing.assert_allclose(L, L0, atol=1e-12)
+    Oa, _ = orc.forward(q, k, np.abs(v), 0.2, causal=True)     # sum_j P_j |V_j| / l
+    t = np.float32(0.2) * np.einsum("bhid,bhjd->bhij", q, k) / math.log(2.0)
+    t = np.where(np.tril(np.ones((N, N), bool)), t, -np.inf)
+    m = np.ceil(t.max(-1))
+    l = np.exp2(t - m[..., None]).sum(-1)
+    csum = np.cumsum(np.abs(v), axis=2)                          # causal sum_j |V_j|
+    bound = desc[2] * (2.0 ** -4 * Oa + 2.0 ** -10 * csum / l[..., None])
+    assert (np.abs(O - O0) <= bound + 1e-12).all()
+    assert np.abs(O - O0).max() > 0                              # the rounding is there
+
+
+def test_planted_fp8_mistakes_are_caught():
+    # Truncation instead of nearest rounding, and a forgotten descale_v, each change the
+    # result the brute-force pin fixes. (A floor instead of a ceiling for the reference is
+    # no mistake: any power-of-two reference rounds the same in the normal range.)
+    N, d = 13, 8
+    q8, k8, v8 = _fp8_codes((N, d), 133), _fp8_codes((N, d), 134), _fp8_codes((N, d), 135)
+    ref, _ = orc.head_forward_fp8(q8, k8, v8, (0.75, 1.25, 0.5), 0.6, causal=True)
+    orig_round, orig_ceil = orc.e4m3_round, np.ceil
+    try:
+        orc.e4m3_round = lambda x: np.sign(x) * np.floor(np.abs(x) * 8) / 8  # truncation-ish
+        bad, _ = orc.head_forward_fp8(q8, k8, v8, (0.75, 1.25, 0.5), 0.6, causal=True)
+        assert np.abs(bad - ref).max() > 1e-6
+    finally:
+        orc.e4m3_round = orig_round
+    bad, _ = orc.head_forward_fp8(q8, k8, v8, (0.75, 1.25, 1.0), 0.6, causal=True)
+    assert np.abs(bad - ref).max() > 1e-6
