@@ -48,6 +48,9 @@ _SIGNATURES = {
                             _U64, _U32, _P]),
     "fa_bwd_dropout": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
                             _P, _I, _I, _F, _U64, _U32, _P, _P]),
+    "fa_fwd_fp8_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _I, _P, _P, _I, _I,
+                        _P, _P]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -224,6 +227,22 @@ def fa_bwd_dropout(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, ca
                                 _stream_ptr(stream)), "fa_bwd_dropout")
 
 
+def fa_fwd_fp8_workspace_bytes(B, H, N, d):
+    return int(lib().fa_fwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, B, H, N, d, scale, descale_q, descale_k, descale_v,
+               causal=0, blockmask=None, kv_len=None, window_left=-1, window_right=-1,
+               workspace=None, stream=None):
+    _check(lib().fa_fwd_fp8(_dev_ptr(q8, "q"), _dev_ptr(k8, "k"), _dev_ptr(v8, "v"),
+                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
+                            float(descale_q), float(descale_k), float(descale_v),
+                            int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
+                            _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
+                            _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
+           "fa_fwd_fp8")
+
+
 # ------------------------------------------------- allocating convenience layer
 
 def _is_f16(t):
@@ -272,3 +291,20 @@ def backward(q, k, v, o, lse, dO, scale, causal=False, blockmask=None, kv_len=No
     fn(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask, kv_len, wl, wr,
        workspace, stream)
     return dq, dk, dv
+
+
+def forward_fp8(q8, k8, v8, scale, descale, causal=False, blockmask=None, kv_len=None,
+                window=None, stream=None):
+    """q8, k8, v8: uint8 GPU tensors [B, H, N, d] of E4M3 codes; descale = (descale_q,
+    descale_k, descale_v). Returns (o bf16, lse fp32), newly allocated (plus a transient
+    workspace for V transposed)."""
+    import torch
+    B, H, N, d = q8.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    ws = torch.empty(max(fa_fwd_fp8_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
+                     device=q8.device)
+    wl, wr = (-1, -1) if window is None else window
+    fa_fwd_fp8(q8, k8, v8, o, lse, B, H, N, d, scale, *descale, causal, blockmask, kv_len, wl,
+               wr, ws, stream)
+    return o, lse

@@ -75,7 +75,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the problem must fit 32-bit indexing)";
     case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: multiples of 8 from 8 to 128)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse/delta 4, workspace 256)";
-    case FA_ERR_SCALE: return "scale must be finite and nonzero";
+    case FA_ERR_SCALE: return "scale must be finite and nonzero (FP8 descales finite and positive)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
@@ -310,6 +310,67 @@ int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* 
            void* workspace, void* stream) {
   return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, blockmask,
                    nullptr, workspace, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ FP8 forward
+
+namespace {
+
+size_t fp8_vt_bytes(int B, int H, int N, int d) {
+  return (size_t)B * H * d * round_up((size_t)N, 64);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK || (d != 64 && d != 128)) return 0;
+  return fp8_vt_bytes(B, H, N, d);
+}
+
+int fa_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, fa_bf16* o, float* lse,
+               int B, int H, int N, int d, float scale, float descale_q, float descale_k,
+               float descale_v, int causal, const uint8_t* blockmask, const int32_t* kv_len,
+               int window_left, int window_right, void* workspace, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 256) || (kv_len && !aligned(kv_len, 4)))
+    return FA_ERR_ALIGN;
+  const size_t ibytes = (size_t)B * H * N * d, lbytes = (size_t)B * H * N * 4;
+  const Range ro = span(o, 2 * ibytes), rl = span(lse, lbytes),
+              rw = span(workspace, fp8_vt_bytes(B, H, N, d));
+  if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw)) return FA_ERR_ALIAS;
+  for (const void* in : {(const void*)q, (const void*)k, (const void*)v}) {
+    const Range ri = span(in, ibytes);
+    if (overlap(ro, ri) || overlap(rl, ri) || overlap(rw, ri)) return FA_ERR_ALIAS;
+  }
+
+  fa::Fp8Params p;
+  p.q = q; p.k = k; p.vt = static_cast<const uint8_t*>(workspace);
+  p.o = o; p.lse = lse;
+  p.blockmask = blockmask;
+  p.kv_len = kv_len;
+  p.B = B; p.H = H; p.N = N;
+  p.Np = (int)round_up((size_t)N, 64);
+  p.sc = std::fabs(scale) * descale_q * descale_k * fa::kLog2eHost;
+  p.qsign = scale < 0.f ? 0x80808080u : 0u;
+  p.descale_v = descale_v;
+  p.causal = causal ? 1 : 0;
+  p.wl = clamp_window(window_left, N);
+  p.wr = clamp_window(window_right, N);
+  if (fa::launch_fwd_fp8(p, v, static_cast<uint8_t*>(workspace), d,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  return FA_OK;
 }
 
 }  // extern "C"

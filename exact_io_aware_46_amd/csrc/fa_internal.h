@@ -54,6 +54,26 @@ struct BwdParams {
   uint32_t seed_lo, seed_hi, drop_offset;
 };
 
+// FP8 forward: Q, K as E4M3 codes [B][H][N][d], V transposed to [B][H][d][Np] (Np = N
+// rounded up to 64, zero past N), O bf16, LSE fp32.
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* vt;
+  uint16_t* o;
+  float* lse;
+  const uint8_t* blockmask;
+  const int32_t* kv_len;
+  int B, H, N, Np;
+  float sc;         // |scale| * descale_q * descale_k * log2(e)
+  uint32_t qsign;   // 0x80808080 for a negative scale (flips the sign of every Q byte)
+  float descale_v;
+  int causal;
+  int wl, wr;       // sliding window as in FwdParams
+};
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
 // Element type of the 16-bit tensors.
 constexpr int kBf16 = 0;
 constexpr int kF16 = 1;
@@ -65,5 +85,8 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
                                  float* delta, float* lse2, int rows, int d, float dsign,
                                  int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream);
+// Transposes v into vt (p.vt), then runs the FP8 forward.
+hipError_t launch_fwd_fp8(const Fp8Params& p, const uint8_t* v, uint8_t* vt, int d,
+                          hipStream_t stream);
 
 }  // namespace fa

@@ -13,7 +13,9 @@ Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
   1. draw Q, K, V, dO in that order with ``standard_normal(dtype=float32)``,
      C-order ``[B][H][N][d]``;
   2. round each float32 to bf16 with round-to-nearest-even on the bit pattern (or, for an
-     fp16 workload, to IEEE binary16 with numpy's round-to-nearest-even conversion);
+     fp16 workload, to IEEE binary16 with numpy's round-to-nearest-even conversion; for an
+     FP8 workload, Q, K, V only, each scaled by its own descale = max|x| / 448 and rounded
+     to E4M3 codes by torch's float8_e4m3fn conversion);
   3. then, if the workload has one, draw the mask input:
      key padding: ``integers(128, 513, size=B)`` (valid length per sequence);
      block mask:  all diagonal blocks kept, plus a uniform draw without replacement
@@ -43,6 +45,24 @@ def f32_to_f16(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
 
 
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values (|x| <= 448) to OCP E4M3 codes (uint8), nearest even, with
+    torch's float8_e4m3fn conversion."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def quantize_e4m3(x: np.ndarray) -> tuple:
+    """Per-tensor FP8 quantisation of float32 values: descale = float32(max|x| / 448)
+    (the largest magnitude maps to the largest finite code), codes = E4M3(x / descale).
+    Returns (codes, descale)."""
+    amax = float(np.abs(x).max())
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    y = np.clip(x / np.float32(descale), -448.0, 448.0).astype(np.float32)
+    return f32_to_e4m3(y), descale
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32 (used by generators and tests to
     look at inputs; both compute paths do their own widening)."""
@@ -62,7 +82,8 @@ class Workload:
     density: float = 1.0        # kept fraction of 128x128 blocks for mask == "block"
     seed: int = 0
     window: tuple | None = None  # sliding window (left, right); negative = no limit
-    dtype: str = "bf16"          # element type of Q, K, V, dO: "bf16" (uint16 bits) or "f16"
+    dtype: str = "bf16"          # element type of Q, K, V, dO: "bf16" (uint16 bits), "f16",
+                                 # or "fp8" (E4M3 codes with per-tensor descales; forward only)
     dropout: tuple | None = None  # attention dropout (p, seed, offset); None = no dropout
 
     @property
@@ -77,7 +98,8 @@ class Workload:
 # The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
 # BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, the long
 # head set with a sliding window, the long causal head set in fp16, the long causal head
-# set with attention dropout, and the long causal head set at head dims 96 and 32.
+# set with attention dropout, the long causal head set at head dims 96 and 32, and the long
+# causal head set in FP8.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -104,6 +126,9 @@ WORKLOADS = {
                                     seed=46009),
     "long_causal_16k_d32": Workload("long_causal_16k_d32", 1, 16, 16384, 32, causal=True,
                                     seed=46010),
+    # The long causal head set in FP8 (E4M3 with per-tensor descales; forward only).
+    "long_causal_16k_fp8": Workload("long_causal_16k_fp8", 1, 16, 16384, 128, causal=True,
+                                    seed=46011, dtype="fp8"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -118,6 +143,7 @@ class Inputs:
     do: np.ndarray
     kv_len: np.ndarray | None = None      # int32 [B]
     blockmask: np.ndarray | None = None   # uint8 [nb][nb], nb = ceil(N/128)
+    descale: tuple | None = None          # fp8: (descale_q, descale_k, descale_v)
 
 
 def n_blocks(n: int) -> int:
@@ -141,11 +167,17 @@ def draw_block_mask(rng: np.random.Generator, n: int, density: float) -> np.ndar
 def make_inputs(wl: Workload, need_do: bool = True) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(wl.seed))
     shape = (wl.B, wl.H, wl.N, wl.d)
-    cvt = f32_to_f16 if wl.dtype == "f16" else f32_to_bf16_bits
-    q = cvt(rng.standard_normal(shape, dtype=np.float32))
-    k = cvt(rng.standard_normal(shape, dtype=np.float32))
-    v = cvt(rng.standard_normal(shape, dtype=np.float32))
-    do = cvt(rng.standard_normal(shape, dtype=np.float32)) if need_do else None
+    descale = None
+    if wl.dtype == "fp8":
+        (q, dq), (k, dk), (v, dv) = (quantize_e4m3(rng.standard_normal(shape, dtype=np.float32))
+                                     for _ in range(3))
+        descale, do = (dq, dk, dv), None
+    else:
+        cvt = f32_to_f16 if wl.dtype == "f16" else f32_to_bf16_bits
+        q = cvt(rng.standard_normal(shape, dtype=np.float32))
+        k = cvt(rng.standard_normal(shape, dtype=np.float32))
+        v = cvt(rng.standard_normal(shape, dtype=np.float32))
+        do = cvt(rng.standard_normal(shape, dtype=np.float32)) if need_do else None
     kv_len = None
     blockmask = None
     if wl.mask == "kpad":
@@ -153,7 +185,7 @@ def make_inputs(wl: Workload, need_do: bool = True) -> Inputs:
         kv_len = np.minimum(kv_len, wl.N).astype(np.int32)
     elif wl.mask == "block":
         blockmask = draw_block_mask(rng, wl.N, wl.density)
-    return Inputs(wl, q, k, v, do, kv_len, blockmask)
+    return Inputs(wl, q, k, v, do, kv_len, blockmask, descale)
 
 
 def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal",

@@ -171,6 +171,33 @@ int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const
                    const int32_t* kv_len, int window_left, int window_right, float dropout_p,
                    uint64_t seed, uint32_t offset, void* workspace, void* stream);
 
+/* FP8 forward (E4M3 inputs). FlashAttention-3 brought FP8 to the forward pass
+ * ("IO感知计算如何重塑Transformer内存优化技术格局", bxzpzcl.cn, section 技术演进时间线); the
+ * pages give no quantisation policy. This one is used:
+ *   q, k, v: DEVICE, OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *     subnormals; S.1111.111 is NaN; largest finite 448), [B][H][N][d] row-major, one
+ *     byte per element; the values are descale_q * q, descale_k * k, descale_v * v.
+ *   S = scale * (descale_q q)(descale_k k)^T, masked as in fa_fwd_window. In log2 units the
+ *     probabilities are P = 2^(S log2(e) - m) for an integer reference m of the row. Each
+ *     P is rounded to E4M3 (nearest, ties to even) for the product with V, and the
+ *     normaliser is the sum of the unrounded P. m is the row's running maximum rounded up,
+ *     so the rounded P equal, up to a power of two, those of the reference
+ *     m = ceil(row max) wherever both lie in the E4M3 normal range.
+ *   o: DEVICE bf16 [B][H][N][d] = descale_v * (rounded P) v / normaliser; lse: DEVICE fp32
+ *     [B][H][N], the natural-log logsumexp of the scores (-inf for a row with no allowed
+ *     key, whose o is 0).
+ *   workspace: DEVICE, 256-byte aligned, fa_fwd_fp8_workspace_bytes(B, H, N, d) bytes:
+ *     receives v transposed to [B][H][d][N rounded up to 64] (zero past N).
+ *   d must be 64 or 128; scale finite and nonzero; each descale finite and > 0.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D, FA_ERR_SCALE, FA_ERR_ALIGN
+ * (q, k, v, o 16 bytes, lse and kv_len 4, workspace 256), FA_ERR_ALIAS (o, lse, workspace
+ * overlapping each other or q, k, v), FA_ERR_LAUNCH. */
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
+int fa_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, fa_bf16* o, float* lse,
+               int B, int H, int N, int d, float scale, float descale_q, float descale_k,
+               float descale_v, int causal, const uint8_t* blockmask, const int32_t* kv_len,
+               int window_left, int window_right, void* workspace, void* stream);
+
 /* Static description of a status code. */
 const char* fa_strerror(int status);
 

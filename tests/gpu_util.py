@@ -120,3 +120,62 @@ def check_all(res, ref, what="", grads=True, o_rel_slack=0.0):
         for name in ("dQ", "dK", "dV"):
             out[name] = check_grad(res[name], ref[name], name, what)
     return out
+
+
+# ------------------------------------------------------------------ FP8 forward
+
+def run_fp8(q8, k8, v8, scale, descale, causal=False, blockmask=None, kv_len=None,
+            window=None):
+    """Runs fa_fwd_fp8 on uint8 code arrays; returns (O, LSE) as float64 and the device
+    workspace (V transposed)."""
+    B, H, N, d = q8.shape
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, k, v = dev(q8), dev(k8), dev(v8)
+    bm = None if blockmask is None else dev(np.asarray(blockmask, dtype=np.uint8))
+    kv = None if kv_len is None else dev(np.asarray(kv_len, dtype=np.int32))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_fwd_fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device="cuda")
+    wl, wr = (-1, -1) if window is None else window
+    fa.fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, *descale, causal, bm, kv, wl, wr, ws)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse), ws
+
+
+def fp8_rounding_bound(q8, k8, v8, descale, scale, O_ref, rows_of, allowed_of):
+    """Elementwise bound on |O_kernel - O_oracle| for the FP8 forward. Both round
+    P = 2^(t - m) to E4M3 against integer references that differ by a power of two 2^k
+    (k >= 0, the kernel's reference is the lower one):
+      - in the normal range the two roundings agree after scaling, except where fp32
+        scores put P on the other side of a rounding tie: at most one E4M3 step,
+        2^-3 P;
+      - where the oracle's P is below 2^-6 (subnormal for it) the two differ by at most
+        2^-9 on the oracle's scale (half a subnormal step each).
+    So |dO| <= descale_v (2^-3 sum_j P_j |V_j| + 2^-9 sum_{P_j < 2^-6} |V_j|) / l, plus the
+    bf16 rounding of O (2^-8 |O| with slack) and 1e-4 for fp32 accumulation.
+    rows_of(b, h) -> query indices of the rows in O_ref[b, h]; allowed_of(b, h, rows) ->
+    boolean [rows][N]."""
+    from oracle import attention as orc
+    dq, dk, dv = (float(np.float32(x)) for x in descale)
+    s = float(np.float32(scale))
+    bound = np.zeros_like(O_ref)
+    B, H = q8.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            rows = rows_of(b, h)
+            if len(rows) == 0:
+                continue
+            Q = dq * orc.e4m3_decode(q8[b, h][rows])
+            K = dk * orc.e4m3_decode(k8[b, h])
+            Va = np.abs(orc.e4m3_decode(v8[b, h]))
+            ok = allowed_of(b, h, rows)
+            t = np.where(ok, s * (Q @ K.T) / np.log(2.0), -np.inf)
+            live = ok.any(axis=1)
+            m = np.ceil(np.where(live, t.max(axis=1), 0.0))
+            P = np.where(ok, np.exp2(t - m[:, None]), 0.0)
+            l = np.where(live, P.sum(axis=1), 1.0)
+            big = (2.0 ** -3) * (P @ Va) / l[:, None]
+            sub = (2.0 ** -9) * (np.where(ok & (P < 2.0 ** -6), 1.0, 0.0) @ Va) / l[:, None]
+            bound[b, h] = dv * (big + sub)
+    return bound + 2.0 ** -8 * np.abs(O_ref) + 1e-4

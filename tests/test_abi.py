@@ -40,7 +40,8 @@ def test_library_exports_exactly_the_header(lib):
     assert decl == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_ex", "fa_bwd_f16",
                     "fa_bwd_preprocess", "fa_bwd_preprocess_f16", "fa_bwd_window",
                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_dropout", "fa_fwd_ex",
-                    "fa_fwd_f16", "fa_fwd_window", "fa_strerror"]
+                    "fa_fwd_f16", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes", "fa_fwd_window",
+                    "fa_strerror"]
     assert exported_functions() == decl
     for name in decl:
         assert hasattr(lib, name)
@@ -189,3 +190,27 @@ def test_dropout_entry_points_validate(lib):
     assert bwd(0, 0.1, None) == 1               # FA_ERR_NULL
     assert bwd(5, 0.1, p[0]) == 9
     assert bwd(1, 1.5, p[0]) == 8
+
+
+def test_fp8_entry_point_validates(lib):
+    p = ptrs(5)
+    ws = A + 64 * T_BYTES
+
+    def call(q=p[0], N=64, d=128, scale=0.1, desc=(0.01, 0.02, 0.03), o=p[3], w=ws):
+        return lib.fa_fwd_fp8(q, p[1], p[2], o, p[4], 1, 2, N, d, scale, *desc, 1, None, None,
+                              -1, -1, w, None)
+    assert call(q=None) == 1                                   # FA_ERR_NULL
+    assert call(w=None) == 1
+    assert call(N=0) == 2                                      # FA_ERR_SHAPE
+    for d in (32, 96, 72, 256):                                # FP8: 64 and 128 only
+        assert call(d=d) == 3
+    assert call(scale=0.0) == 5                                # FA_ERR_SCALE
+    for desc in ((0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, float("nan")),
+                 (float("inf"), 1.0, 1.0)):
+        assert call(desc=desc) == 5
+    assert call(q=p[0] + 8) == 4                               # FA_ERR_ALIGN
+    assert call(w=ws + 16) == 4
+    assert call(o=p[0]) == 7                                   # o overlaps q
+    assert call(w=p[2]) == 7                                   # workspace overlaps v
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 100, 128) == 2 * 128 * 128  # N -> 128
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 100, 96) == 0

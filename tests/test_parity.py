@@ -13,7 +13,8 @@ import torch
 
 from exact_io_aware_46_amd import inputs as inp
 from oracle import attention as orc
-from tests.gpu_util import Run, check_all, check_grad, check_lse, check_o, say, to_dev, to_f64
+from tests.gpu_util import (Run, check_all, check_grad, check_lse, check_o, fp8_rounding_bound,
+                            run_fp8, say, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -568,3 +569,138 @@ def test_padded_head_dim_writes_nothing_past_its_outputs(d):
     torch.cuda.synchronize()
     for name, b in bufs.items():
         assert (b[n:] == 0x5A5A).all().item(), f"{name} written past its end"
+
+
+# ------------------------------------------------------------------ FP8 forward
+
+def _fp8_inputs(B, H, N, d, seed, sd=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, desc = [], []
+    for _ in range(3):
+        c, ds = inp.quantize_e4m3((sd * rng.standard_normal((B, H, N, d))).astype(np.float32))
+        out.append(c)
+        desc.append(ds)
+    return out[0], out[1], out[2], tuple(desc)
+
+
+def _fp8_coarse_inputs(B, H, N, d, seed):
+    """Q and K codes from {0, +-0.5, +-1, +-1.5, +-2} (descale 1/4 and 1/2), V from N(0, 1):
+    every score is a short dyadic sum that the matrix unit adds exactly, so kernel and
+    oracle see the same scores up to one fp32 rounding of the scale. (With full-mantissa
+    codes the FP8 matrix unit's sums are about 2^-15 relative off exact, which moves P
+    across E4M3 rounding ties now and then; the bound tests cover that case.)"""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    grid = np.array([-2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2], dtype=np.float32)
+    q = grid[rng.integers(0, 9, (B, H, N, d))]
+    k = grid[rng.integers(0, 9, (B, H, N, d))]
+    v8, dv = inp.quantize_e4m3(rng.standard_normal((B, H, N, d)).astype(np.float32))
+    return inp.f32_to_e4m3(4 * q), inp.f32_to_e4m3(2 * k), v8, (0.25, 0.5, dv)
+
+
+def _fp8_check_tight(O, L, ref_O, ref_L, what):
+    check_o(O, ref_O, what)
+    check_lse(L, ref_L, what)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,scale", [(1, False, 0.09), (7, True, 0.09), (40, False, -0.11),
+                                            (64, True, 0.2), (64, False, 0.05)])
+def test_fp8_single_tile_matches_the_quantised_oracle(d, N, causal, scale):
+    """One key tile: the kernel's reference max is the row max rounded up, the oracle's
+    reference, so (with exactly summed scores) every P rounds the same on both sides."""
+    q8, k8, v8, desc = _fp8_coarse_inputs(2, 2, N, d, seed=151 + N)
+    say(f"[parity] fp8 single tile d={d} N={N} causal={causal} scale={scale}")
+    O, L, _ = run_fp8(q8, k8, v8, scale, desc, causal)
+    ref_O, ref_L = orc.forward_fp8(q8, k8, v8, desc, scale, causal)
+    _fp8_check_tight(O, L, ref_O, ref_L, f"fp8 d={d} N={N}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,kv", [(300, True, None), (700, False, [700, 333])])
+def test_fp8_sink_key_makes_every_tile_match_the_quantised_oracle(d, N, causal, kv):
+    """Key 0 holds every row's maximum score (a large first component on key 0 and on every
+    query), so the first tile sets the reference and later tiles never raise it: the
+    kernel quantises exactly the oracle's P across many tiles."""
+    B = 1 if kv is None else len(kv)
+    rng = np.random.Generator(np.random.PCG64(157 + N))
+    grid = np.array([-1, -0.5, 0, 0.5, 1], dtype=np.float32)
+    q = grid[rng.integers(0, 5, (B, 2, N, d))]
+    k = grid[rng.integers(0, 5, (B, 2, N, d))]
+    v8, dv = inp.quantize_e4m3(rng.standard_normal((B, 2, N, d)).astype(np.float32))
+    q[..., 0] = 2.0
+    k[..., 0] = 0.0
+    k[:, :, 0, 0] = 64.0
+    q8, k8 = inp.f32_to_e4m3(q), inp.f32_to_e4m3(k)
+    desc, scale = (1.0, 1.0, dv), 0.02
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    say(f"[parity] fp8 sink d={d} N={N} causal={causal} kv={kv}")
+    O, L, _ = run_fp8(q8, k8, v8, scale, desc, causal, None, kvn)
+    ref_O, ref_L = orc.forward_fp8(q8, k8, v8, desc, scale, causal, None, kvn)
+    _fp8_check_tight(O, L, ref_O, ref_L, f"fp8 sink d={d}")
+
+
+def _fp8_bound_check(O, L, q8, k8, v8, desc, scale, causal, bm, kv, window, what):
+    ref_O, ref_L = orc.forward_fp8(q8, k8, v8, desc, scale, causal, bm, kv, window)
+    check_lse(L, ref_L, what)
+    N = q8.shape[2]
+    bound = fp8_rounding_bound(
+        q8, k8, v8, desc, scale, ref_O, lambda b, h: np.arange(N),
+        lambda b, h, rows: orc.allowed(rows, N, causal, bm, None if kv is None else int(kv[b]),
+                                       window))
+    err = np.abs(O - ref_O)
+    say(f"   {what}: max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}, "
+        f"rel-L2 {np.linalg.norm(O - ref_O) / np.linalg.norm(ref_O):.3e}")
+    assert (err <= bound).all(), f"{what} outside the FP8 rounding bound"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal,window,kv,bm", [
+    (129, False, None, None, None),
+    (300, True, None, None, None),
+    (300, False, (60, 20), None, None),
+    (384, True, None, [384, 150], [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
+])
+def test_fp8_within_the_rounding_bound(d, N, causal, window, kv, bm):
+    B = 1 if kv is None else len(kv)
+    q8, k8, v8, desc = _fp8_inputs(B, 2, N, d, seed=163 + N + d)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    bmn = None if bm is None else np.array(bm, dtype=np.uint8)
+    scale = float(np.float32(d ** -0.5))
+    say(f"[parity] fp8 bound d={d} N={N} causal={causal} window={window} kv={kv}")
+    O, L, _ = run_fp8(q8, k8, v8, scale, desc, causal, bmn, kvn, window)
+    _fp8_bound_check(O, L, q8, k8, v8, desc, scale, causal, bmn, kvn, window,
+                     f"fp8 d={d} N={N}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_transposed_v_workspace_is_exact_and_outputs_deterministic(d):
+    N = 200                                     # padded to 256 columns in the workspace
+    q8, k8, v8, desc = _fp8_inputs(1, 3, N, d, seed=167)
+    say(f"[bitexact] fp8 V^T workspace d={d}")
+    O, L, ws = run_fp8(q8, k8, v8, 0.1, desc, True)
+    Np = 256
+    vt = ws.cpu().numpy().reshape(1, 3, d, Np)
+    assert np.array_equal(vt[..., :N], np.swapaxes(v8, 2, 3))
+    assert (vt[..., N:] == 0).all()
+    O2, L2, _ = run_fp8(q8, k8, v8, 0.1, desc, True)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_fp8_workload_sampled_rows():
+    wl = inp.WORKLOADS["long_causal_16k_fp8"]
+    x = inp.make_inputs(wl)
+    say("[parity] long_causal_16k_fp8 (sampled rows)")
+    O, L, _ = run_fp8(x.q, x.k, x.v, wl.scale, x.descale, wl.causal)
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    sel = _sample_rows(wl, 24, wl.seed)
+    o_ref, l_ref = orc.forward_fp8_rows(x.q, x.k, x.v, x.descale, wl.scale, sel, wl.causal)
+    idx = tuple(np.array(sel).T)
+    check_lse(L[idx], l_ref, "fp8 workload")
+    for n, (b, h, i) in enumerate(sel):
+        one = fp8_rounding_bound(
+            x.q[b:b + 1, h:h + 1], x.k[b:b + 1, h:h + 1], x.v[b:b + 1, h:h + 1], x.descale,
+            wl.scale, o_ref[n][None, None, None],
+            lambda bb, hh: np.array([i]),
+            lambda bb, hh, rows: orc.allowed(rows, wl.N, wl.causal, None, None))
+        err = np.abs(O[b, h, i] - o_ref[n])
+        assert (err <= one[0, 0, 0]).all(), f"row {(b, h, i)}: {err.max():.3e}"
