@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd and fwd+bwd (bf16) at 1 GPU + % MFMA peak"
 
@@ -139,6 +140,82 @@ class Buffers:
         self.bwd()
 
 
+class Fp8Buffers:
+    """Device buffers of the FP8 forward (E4M3 Q, K, V; bf16 O; V^T workspace)."""
+
+    def __init__(self, x, torch):
+        import exact_io_aware_46_amd as fa
+        wl = x.wl
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.wl, self.fa, self.descale = wl, fa, x.descale
+        self.q, self.k, self.v = dev(x.q), dev(x.k), dev(x.v)
+        self.o = torch.empty((wl.B, wl.H, wl.N, wl.d), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(fa.fa_fwd_fp8_workspace_bytes(wl.B, wl.H, wl.N, wl.d),
+                              dtype=torch.uint8, device="cuda")
+        self.bm = None if x.blockmask is None else torch.from_numpy(x.blockmask).cuda()
+        self.kv = None if x.kv_len is None else torch.from_numpy(x.kv_len).cuda()
+
+    def fwd(self):
+        w = self.wl
+        wl, wr = (-1, -1) if w.window is None else w.window
+        self.fa.fa_fwd_fp8(self.q, self.k, self.v, self.o, self.lse, w.B, w.H, w.N, w.d,
+                           w.scale, *self.descale, w.causal, self.bm, self.kv, wl, wr, self.ws)
+
+
+def fp8_cpu_baseline(x, heads=2):
+    """The FP8 oracle forward (as it stands) on the first ``heads`` heads; rate =
+    4 * pairs * d FLOP / wall time."""
+    import threadpoolctl
+    from oracle import attention as orc
+    wl = x.wl
+    sel = [(b, h) for b in range(wl.B) for h in range(wl.H)][:heads]
+    flop = 0.0
+    t0 = time.perf_counter()
+    for b, h in sel:
+        kv = None if x.kv_len is None else int(x.kv_len[b])
+        orc.head_forward_fp8(x.q[b, h], x.k[b, h], x.v[b, h], x.descale, wl.scale, wl.causal,
+                             x.blockmask, kv, window=wl.window)
+        flop += 4.0 * allowed_pairs(wl.N, wl.causal, x.blockmask, kv, wl.window) * wl.d
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(sel)} of {wl.B * wl.H} heads of {wl.name} (N={wl.N}, d={wl.d}): "
+                      f"fp64 FP8-quantised forward with S and P materialised, numpy/OpenBLAS, "
+                      f"{dt:.1f} s wall"}
+
+
+def fp8_main(args, torch, wl, x):
+    """FP8 workloads are forward only: a step is one forward (the V transpose pass
+    included)."""
+    pairs = workload_pairs(x)
+    fl_fwd = 4.0 * pairs * wl.d
+    buf = Fp8Buffers(x, torch)
+    ms_fwd = time_loop(torch, buf.fwd, args.steps, args.warmup)
+    tf_fwd = fl_fwd / (ms_fwd * 1e-3) / 1e12
+    k_fwd = f"fwd_fp8_kernel<{wl.d}>"
+    rec = {
+        "metric": "attention TFLOP/s fwd (fp8 e4m3 inputs) at 1 GPU + % MFMA peak",
+        "value": round(tf_fwd, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_fwd, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "causal": wl.causal, "mask": wl.mask, "window": wl.window,
+                   "scale": wl.scale, "descale": list(x.descale), "allowed_pairs": pairs},
+        "fwd_tflops": round(tf_fwd, 2), "fwd_ms": round(ms_fwd, 4),
+        "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_FP8_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": f"{k_fwd} + vt_fp8_kernel<{wl.d}> (whole forward)",
+                     "bound": "mfma", "achieved": round(tf_fwd, 2),
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_fwd / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, "fp8_kernel", [k_fwd])},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = fp8_cpu_baseline(x)
+    print(json.dumps(rec), flush=True)
+
+
 def time_loop(torch, fn, steps, warmup):
     """Mean milliseconds per call, HIP events on the stream the kernels run on."""
     for _ in range(warmup):
@@ -183,7 +260,8 @@ def footprint_sweep(torch, base):
 
 
 KERNEL_SOURCES = {"fwd_kernel": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.h"],
-                  "bwd_kernel": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.h"]}
+                  "bwd_kernel": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.h"],
+                  "fp8_kernel": ["fa_fwd_fp8.hip", "fa_device.hpp", "fa_internal.h"]}
 
 
 def source_hash(kind):
@@ -259,6 +337,9 @@ def main():
         del src, dst
     wl = inp.WORKLOADS[args.workload]
     x = inp.make_inputs(wl)
+    if wl.dtype == "fp8":
+        fp8_main(args, torch, wl, x)
+        return
     pairs = workload_pairs(x)
     fl_fwd, fl_bwd = 4.0 * pairs * wl.d, 10.0 * pairs * wl.d
     buf = Buffers(x, torch)
