@@ -185,7 +185,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + acc_row(i, hi);
-          const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
+          const bool ok = (key < klim) & (key <= myq + rl) & (key >= myq - ll);
           if (!ok) s[kb][i] = -kInf;
         }
     }

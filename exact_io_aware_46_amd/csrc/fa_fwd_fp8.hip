@@ -227,7 +227,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + 16 * hi + i;
-          const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
+          const bool ok = (key < klim) & (key <= myq + rl) & (key >= myq - ll);
           if (!ok) s[kb][i] = -kInf;
         }
     }
