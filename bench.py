@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--workload", default="long_causal_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-footprint", action="store_true")
+    ap.add_argument("--no-device-sample", action="store_true",
+                    help="skip the amd-smi clock/power sample (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a kernel of known "
                          "traffic, used to scale hardware byte counters)")
@@ -211,9 +213,41 @@ def fp8_main(args, torch, wl, x):
                      "frac": round(tf_fwd / MFMA_FP8_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name, "fp8_kernel", [k_fwd])},
     }
+    rec["device"] = None if args.no_device_sample else device_sample(torch, buf.fwd)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = fp8_cpu_baseline(x)
     print(json.dumps(rec), flush=True)
+
+
+def device_sample(torch, fn, seconds=5.0):
+    """Clock and power while the GPU runs ``fn`` back to back: one ``amd-smi metric`` query
+    in a child process, sampled while the steps run. Returns None if amd-smi is missing or
+    fails."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        proc = subprocess.Popen([exe, "metric", "-c", "-p", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=max(1.0, seconds - (time.perf_counter() - t0)))
+        gpu = json.loads(out)["gpu_data"][0]
+        clks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and "clk" in v]
+        return {"gfx_clk_mhz_mean": round(sum(clks) / len(clks), 1), "gfx_clk_mhz": clks,
+                "socket_power_w": gpu["power"]["socket_power"]["value"],
+                "source": "amd-smi metric -c -p, sampled while steps ran"}
+    except Exception:  # noqa: BLE001 -- the sample is optional context
+        proc.kill()
+        return None
 
 
 def time_loop(torch, fn, steps, warmup):
@@ -388,6 +422,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(wl.name, "fwd_kernel", [k_fwd])},
     }
+    rec["device"] = None if args.no_device_sample else device_sample(torch, buf.step)
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf
         rec["footprint"] = footprint_sweep(torch, wl)
