@@ -28,6 +28,17 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+
+# The pages' own figures, each on its own (NVIDIA) hardware: context, not targets.
+PAGE_CONTEXT = [
+    {"figure": "2-3x speed-up and 10x memory saving over standard attention",
+     "hardware": "A100", "system": "FlashAttention"},
+    {"figure": "175 TFLOP/s at 16K sequence length", "hardware": "A100",
+     "system": "FlashAttention-2"},
+    {"figure": "550 TFLOP/s forward, fp16, head dim 256", "hardware": "H100",
+     "system": "FlashAttention-3"},
+    {"figure": "700 TFLOP/s forward, FP8", "hardware": "H100", "system": "FlashAttention-3"},
+]
 HBM_PEAK_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd and fwd+bwd (bf16) at 1 GPU + % MFMA peak"
 
@@ -214,31 +225,45 @@ def fp8_main(args, torch, wl, x):
                      "traffic": measured_traffic(wl.name, "fp8_kernel", [k_fwd])},
     }
     rec["device"] = None if args.no_device_sample else device_sample(torch, buf.fwd)
+    rec["context"] = {"note": "the pages' figures on their own hardware; context only",
+                      "items": PAGE_CONTEXT}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = fp8_cpu_baseline(x)
     print(json.dumps(rec), flush=True)
 
 
 def device_sample(torch, fn, seconds=5.0):
-    """Clock and power while the GPU runs ``fn`` back to back: one ``amd-smi metric`` query
-    in a child process, sampled while the steps run. Returns None if amd-smi is missing or
+    """Clock and power while the GPU runs ``fn`` back to back: about 0.5 s of steps are
+    queued first (so the clocks have ramped), then one ``amd-smi metric`` query runs in a
+    child process while steps keep the queue full. Returns None if amd-smi is missing or
     fails."""
     import shutil
     import subprocess
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < 0.5:
+        fn()
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
     try:
         proc = subprocess.Popen([exe, "metric", "-c", "-p", "--json"], stdout=subprocess.PIPE,
                                 stderr=subprocess.DEVNULL, text=True)
     except OSError:
-        return None
-    t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < seconds:
-        fn()
         torch.cuda.synchronize()
+        return None
+    t1 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t1 < seconds:
+        fn()
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     try:
-        out, _ = proc.communicate(timeout=max(1.0, seconds - (time.perf_counter() - t0)))
+        out, _ = proc.communicate(timeout=max(1.0, seconds - (time.perf_counter() - t1)))
         gpu = json.loads(out)["gpu_data"][0]
         clks = [v["clk"]["value"] for k, v in gpu["clock"].items()
                 if k.startswith("gfx_") and isinstance(v, dict) and "clk" in v]
@@ -265,8 +290,9 @@ def time_loop(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def footprint_sweep(torch, base):
-    """Peak device bytes of fwd+bwd buffers + workspace + calls at several N (same B, H, d)."""
+def footprint_sweep(torch, base, steps=10, warmup=3):
+    """Peak device bytes of fwd+bwd buffers + workspace + calls at several N (same B, H, d),
+    and the fwd and fwd+bwd TFLOP/s at each N (timed like the main loop)."""
     from exact_io_aware_46_amd import inputs as inp
     out = {}
     for n in (2048, 4096, 8192, 16384):
@@ -284,6 +310,11 @@ def footprint_sweep(torch, base):
         out[str(n)] = {"peak_bytes": int(torch.cuda.max_memory_allocated() - before),
                        "hip_free_delta_bytes": int(free0 - free1),
                        "materialised_SP_bf16_bytes": 2 * wl.B * wl.H * n * n * 2}
+        pairs = workload_pairs(x)
+        ms_f = time_loop(torch, buf.fwd, steps, warmup)
+        ms_s = time_loop(torch, buf.step, steps, warmup)
+        out[str(n)]["fwd_tflops"] = round(4.0 * pairs * wl.d / (ms_f * 1e-3) / 1e12, 2)
+        out[str(n)]["fwd_bwd_tflops"] = round(14.0 * pairs * wl.d / (ms_s * 1e-3) / 1e12, 2)
         del buf
     ns = np.array([int(n) for n in out])
     pk = np.array([out[str(n)]["peak_bytes"] for n in ns], dtype=np.float64)
@@ -423,6 +454,10 @@ def main():
                          "traffic": measured_traffic(wl.name, "fwd_kernel", [k_fwd])},
     }
     rec["device"] = None if args.no_device_sample else device_sample(torch, buf.step)
+    rec["context"] = {"note": "the pages' figures on their own hardware; context only",
+                      "source": "IO感知计算如何重塑Transformer内存优化技术格局 (bxzpzcl.cn), "
+                                "sections 技术演进时间线 and NVIDIA CUDA平台优化",
+                      "items": PAGE_CONTEXT}
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf
         rec["footprint"] = footprint_sweep(torch, wl)
