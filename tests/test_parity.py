@@ -7,6 +7,8 @@ workloads are run in the same launch configuration as the bench; the largest two
 compared on sampled rows (O, LSE, dQ computed row by row by the oracle) and on one
 whole head (dK, dV).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -704,3 +706,44 @@ def test_fp8_workload_sampled_rows():
             lambda bb, hh, rows: orc.allowed(rows, wl.N, wl.causal, None, None))
         err = np.abs(O[b, h, i] - o_ref[n])
         assert (err <= one[0, 0, 0]).all(), f"row {(b, h, i)}: {err.max():.3e}"
+
+
+# ------------------------------------------------ full-size ragged sequence length
+
+def test_long_ragged_length_sampled_rows():
+    """N = 16381 (odd, ragged against every tile size) at the long workload's shape:
+    sampled rows including the last, and the last full head."""
+    wl = dataclasses.replace(inp.WORKLOADS["long_causal_16k"].with_n(16381), H=4)
+    x = inp.make_inputs(wl)
+    say(f"[parity] {wl.name} H=4 (sampled rows + one full head)")
+    res = Run(x.q, x.k, x.v, x.do, wl.scale, wl.causal).result()
+    sel = sorted(set(_sample_rows(wl, 24, 46100)) | {(0, 3, 16380), (0, 0, 16379), (0, 2, 16320)})
+    o_ref, l_ref = orc.forward_rows(x.q, x.k, x.v, wl.scale, sel, wl.causal)
+    dq_ref = orc.dq_rows(x.q, x.k, x.v, x.do, wl.scale, sel, wl.causal)
+    idx = tuple(np.array(sel).T)
+    check_o(res["O"][idx], o_ref, wl.name)
+    check_lse(res["LSE"][idx], l_ref, wl.name)
+    check_grad(res["dQ"][idx], dq_ref, "dQ", wl.name)
+    ref = orc.head_backward(orc.as_f64(x.q[0, 3]), orc.as_f64(x.k[0, 3]), orc.as_f64(x.v[0, 3]),
+                            orc.as_f64(x.do[0, 3]), wl.scale, wl.causal)
+    for g in ("dK", "dV"):
+        check_grad(res[g][0, 3], ref[g], g, wl.name)
+
+
+def test_fp8_long_ragged_length_sampled_rows():
+    wl = dataclasses.replace(inp.WORKLOADS["long_causal_16k_fp8"].with_n(16381), H=2)
+    x = inp.make_inputs(wl)
+    say(f"[parity] {wl.name} H=2 (sampled rows)")
+    O, L, ws = run_fp8(x.q, x.k, x.v, wl.scale, x.descale, wl.causal)
+    sel = sorted(set(_sample_rows(wl, 12, 46101)) | {(0, 1, 16380), (0, 0, 16379)})
+    o_ref, l_ref = orc.forward_fp8_rows(x.q, x.k, x.v, x.descale, wl.scale, sel, wl.causal)
+    idx = tuple(np.array(sel).T)
+    check_lse(L[idx], l_ref, wl.name)
+    for n, (b, h, i) in enumerate(sel):
+        bound = fp8_rounding_bound(
+            x.q[b:b + 1, h:h + 1], x.k[b:b + 1, h:h + 1], x.v[b:b + 1, h:h + 1], x.descale,
+            wl.scale, o_ref[n][None, None, None], lambda bb, hh: np.array([i]),
+            lambda bb, hh, rows: orc.allowed(rows, wl.N, wl.causal, None, None))
+        assert (np.abs(O[b, h, i] - o_ref[n]) <= bound[0, 0, 0]).all(), (b, h, i)
+    vt = ws.cpu().numpy().reshape(1, 2, 128, 16384)
+    assert (vt[..., 16381:] == 0).all()
