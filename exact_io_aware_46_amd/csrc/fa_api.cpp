@@ -22,7 +22,7 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // fit in a signed 32-bit int, and the grid size in a 32-bit unsigned.
 int check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d < 8 || d > 128 || d % 8 != 0) return FA_ERR_UNSUPPORTED_D;
+  if (d < 8 || d > 256 || d % 8 != 0) return FA_ERR_UNSUPPORTED_D;
   const long long rows = (long long)B * H * N;
   if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
   if ((long long)N * d > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -73,7 +73,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and the problem must fit 32-bit indexing)";
-    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: multiples of 8 from 8 to 128)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (supported: multiples of 8 from 8 to 256; FP8: 64, 128)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse/delta 4, workspace 256)";
     case FA_ERR_SCALE: return "scale must be finite and nonzero (FP8 descales finite and positive)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -205,6 +205,7 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
              float dropout_p, uint64_t seed, uint32_t offset, void* workspace, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
+  if (st == FA_OK && d > 128) st = FA_ERR_UNSUPPORTED_D;  // backward: d <= 128
   if (st != FA_OK) return st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||

@@ -582,10 +582,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 template <typename T>
 hipError_t launch_pre_t(const uint16_t* o, const uint16_t* dO, const float* lse, float* delta,
                         float* lse2, int rows, int d, float dsign, hipStream_t stream) {
-  const int dt = d > 64 ? 128 : 64;  // threads per row cover dt columns
+  const int dt = d > 128 ? 256 : d > 64 ? 128 : 64;  // threads per row cover dt columns
   const int rpb = 256 / (dt / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  if (dt == 128)
+  if (dt == 256)
+    hipLaunchKernelGGL((bwd_pre_kernel<T, 256>), grid, dim3(256), 0, stream, o, dO, lse, delta,
+                       lse2, rows, d, dsign);
+  else if (dt == 128)
     hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), grid, dim3(256), 0, stream, o, dO, lse, delta,
                        lse2, rows, d, dsign);
   else

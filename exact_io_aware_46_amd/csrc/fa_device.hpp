@@ -130,9 +130,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //      swz must differ between them.
 // d = 128: swap the two bit pairs of the low row nibble. d = 64: bit 2 from row bit 1,
 // bits 0-1 from row bits 2-3.
+// d = 256 (32 chunks, 512-byte rows spanning two bank windows): chunk c of any row sits in
+// bank group c mod 16, so the d = 128 swizzle on the chunk's low four bits keeps both
+// patterns conflict-free.
 template <int CH>
 __device__ __forceinline__ int swz(int k) {
-  if constexpr (CH == 16) return ((k & 3) << 2) | ((k >> 2) & 3);
+  if constexpr (CH == 16 || CH == 32) return ((k & 3) << 2) | ((k >> 2) & 3);
   else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
 }
 

@@ -34,16 +34,18 @@ namespace {
 // on the 64 / 128 layout: the contraction and the O columns stop at DC, so the unused
 // chunks of each row are never read). PAD: the head dim p.dh is below D (global rows are
 // p.dh wide; the copies skip chunks at or past it).
-template <typename T, int D, int BC, bool DROP, bool PAD, int DC>
-__global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
-  constexpr int BR = 256;           // queries per workgroup (8 waves x 32)
+// NW: waves per workgroup (8, two per SIMD; 4 for d = 256, whose accumulators need the
+// registers of one wave per SIMD).
+template <typename T, int D, int BC, bool DROP, bool PAD, int DC, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
+  constexpr int BR = 32 * NW;       // queries per workgroup (NW waves x 32)
   constexpr int NS = DC / 16;       // contraction steps of the score MFMA
   constexpr int KB = BC / 32;       // 32-key blocks per key tile
   constexpr int DB = DC / 32;       // 32-wide column blocks of O
   constexpr int CH = D / 8;         // 16-byte chunks per row
   constexpr int ROWB = D * 2;       // bytes per row
   constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
-  constexpr int LPW = TILE / 1024 / 8;  // 1 KB wave-wide DMA loads per wave per tile
+  constexpr int LPW = TILE / 1024 / NW;  // 1 KB wave-wide DMA loads per wave per tile
   // Two stages (double buffering) of a K tile and a V tile, both row-major, swizzled.
   // Each stage is its own array so the compiler can tell the tile being read from the one
   // being filled and does not wait for the in-flight copy before reading.
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   // Block table rows of the workgroup's two 128-query blocks (the second may not exist)
   // and of this wave's block.
   const uint8_t* bm0 = p.blockmask ? p.blockmask + (size_t)(q0 >> 7) * nb : nullptr;
-  const uint8_t* bm1 = (bm0 && (q0 >> 7) + 1 < nb) ? bm0 + nb : bm0;
+  const uint8_t* bm1 = (NW == 8 && bm0 && (q0 >> 7) + 1 < nb) ? bm0 + nb : bm0;
   const uint8_t* bmw = (wave < 4) ? bm0 : bm1;
 
   // Next key tile at or after kt that either query block keeps (all without a table).
@@ -127,10 +129,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
 
   if constexpr (PAD && DC == D) {  // padded columns are read: they must hold zeros
-    zero_pad<CH>(sK0, TILE, cha, tid, 512);
-    zero_pad<CH>(sV0, TILE, cha, tid, 512);
-    zero_pad<CH>(sK1, TILE, cha, tid, 512);
-    zero_pad<CH>(sV1, TILE, cha, tid, 512);
+    zero_pad<CH>(sK0, TILE, cha, tid, 64 * NW);
+    zero_pad<CH>(sV0, TILE, cha, tid, 64 * NW);
+    zero_pad<CH>(sK1, TILE, cha, tid, 64 * NW);
+    zero_pad<CH>(sV1, TILE, cha, tid, 64 * NW);
   }
   int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
@@ -291,22 +293,32 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p) {
 
 template <typename T, bool DROP>
 hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
-  const int nqt = (p.N + 255) / 256;
-  const dim3 grid((unsigned)nqt * (unsigned)(p.B * p.H));
+  const unsigned bh = (unsigned)(p.B * p.H);
+  if (d > 128) {  // 256-wide tiles, four waves of 32 queries
+    const dim3 grid((unsigned)((p.N + 127) / 128) * bh);
+    if (d == 256)
+      hipLaunchKernelGGL((fwd_kernel<T, 256, 64, DROP, false, 256, 4>), grid, dim3(256), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, 256, 64, DROP, true, 256, 4>), grid, dim3(256), 0,
+                         stream, p);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((p.N + 255) / 256) * bh);
   // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
   // head dims run the next kernel up on zero-padded tiles.
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false, 128>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false, 128, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 96)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 96>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
   else if (d > 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 128>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 32)
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 32>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 32, 8>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 64, 8>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

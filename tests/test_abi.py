@@ -76,8 +76,8 @@ def test_fwd_bad_shape(lib, B, H, N):
     assert fwd(lib, B=B, H=H, N=N) == 2
 
 
-# Supported: multiples of 8 from 8 to 128.
-@pytest.mark.parametrize("d", [0, 4, 20, 100, 136, 256, -64])
+# Supported: multiples of 8 from 8 to 256 (the backward: up to 128).
+@pytest.mark.parametrize("d", [0, 4, 20, 100, 260, 264, 512, -64])
 def test_fwd_unsupported_head_dim(lib, d):
     assert fwd(lib, d=d) == 3
 
@@ -113,6 +113,7 @@ def test_bwd_errors(lib):
         assert bwd(lib, {i: 0}) == 1
     assert bwd(lib, B=0) == 2
     assert bwd(lib, d=136) == 3
+    assert bwd(lib, d=256) == 3                      # the backward stops at 128
     assert bwd(lib, {0: A + 8}) == 4
     assert bwd(lib, ws_off=16) == 4                  # workspace needs 256-byte alignment
     assert bwd(lib, scale=float("nan")) == 5
@@ -149,7 +150,7 @@ def test_window_entry_points_validate_like_the_others(lib):
     fwd_args = lambda q, d, scale: (q, p[1], p[2], p[3], p[4], 1, 1, 64, d, scale, 0, None,
                                     None, 3, -1, None)
     assert lib.fa_fwd_window(*fwd_args(None, 64, 0.125)) == 1          # FA_ERR_NULL
-    assert lib.fa_fwd_window(*fwd_args(p[0], 200, 0.125)) == 3         # FA_ERR_UNSUPPORTED_D
+    assert lib.fa_fwd_window(*fwd_args(p[0], 260, 0.125)) == 3         # FA_ERR_UNSUPPORTED_D
     assert lib.fa_fwd_window(*fwd_args(p[0], 64, float("nan"))) == 5   # FA_ERR_SCALE
     assert lib.fa_fwd_window(*fwd_args(p[0] + 2, 64, 0.125)) == 4     # FA_ERR_ALIGN
     ws = A + 64 * T_BYTES

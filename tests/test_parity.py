@@ -747,3 +747,35 @@ def test_fp8_long_ragged_length_sampled_rows():
         assert (np.abs(O[b, h, i] - o_ref[n]) <= bound[0, 0, 0]).all(), (b, h, i)
     vt = ws.cpu().numpy().reshape(1, 2, 128, 16384)
     assert (vt[..., 16381:] == 0).all()
+
+
+# ------------------------------------------------------- head dims above 128 (forward)
+
+@pytest.mark.parametrize("d", [256, 200])
+@pytest.mark.parametrize("N,causal,window,kv,bm", [
+    (1, False, None, None, None),
+    (129, True, None, None, None),
+    (300, False, (60, 20), None, None),
+    (384, True, None, [384, 150], [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
+])
+def test_forward_head_dims_above_128(d, N, causal, window, kv, bm):
+    B = 1 if kv is None else len(kv)
+    q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=173 + N + d)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    bmn = None if bm is None else np.array(bm, dtype=np.uint8)
+    scale = float(np.float32(d ** -0.5))
+    say(f"[parity] forward d={d} N={N} causal={causal} window={window} kv={kv}")
+    res = Run(q, k, v, None, scale, causal, bmn, kvn, backward=False, window=window).result()
+    ref_o, ref_l = orc.forward(q, k, v, scale, causal, bmn, kvn, window=window)
+    check_o(res["O"], ref_o, f"d={d}")
+    check_lse(res["LSE"], ref_l, f"d={d}")
+
+
+def test_forward_d200_is_bitwise_d256_on_zero_padded_tensors():
+    N = 300
+    q, k, v, _ = inp.custom_inputs(1, 2, N, 200, seed=179)
+    say("[bitexact] forward d=200 vs 256 zero-padded")
+    a = Run(q, k, v, None, 0.07, True, backward=False)
+    b = Run(*(_zero_pad_cols(x, 256) for x in (q, k, v)), None, 0.07, True, backward=False)
+    assert _bits_equal(a.lse, b.lse)
+    assert _bits_equal(a.o, b.o[..., :200].contiguous())
