@@ -205,7 +205,6 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
              float dropout_p, uint64_t seed, uint32_t offset, void* workspace, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
-  if (st == FA_OK && d > 128) st = FA_ERR_UNSUPPORTED_D;  // backward: d <= 128
   if (st != FA_OK) return st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||

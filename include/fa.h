@@ -43,13 +43,12 @@
  *   global mutable state. Outputs must not alias inputs or each other.
  *   stream: a hipStream_t (NULL = the default stream). All work is enqueued asynchronously
  *   on it; inputs must stay valid and unmodified until the stream has run the work.
- *   Supported head dims: d a multiple of 8 from 8 to 256 (the backward: up to 128; the FP8
- *   forward: 64 and 128). The kernels' tiles are 64, 128 or 256 columns wide (256: four
- *   waves of 32 queries per workgroup, one per SIMD, for the register budget). d = 32 and
- *   96 run on the 64 / 128 tiles but compute only their own width. Any other d runs on
- *   the next tile width up with the extra columns zero-padded: zero columns add nothing
- *   to Q K^T, and the padded output columns are never written. That costs the padded
- *   matrix work.
+ *   Supported head dims: d a multiple of 8 from 8 to 256 (the FP8 forward: 64 and 128).
+ *   The kernels' tiles are 64, 128 or 256 columns wide (256: four waves of 32 queries per
+ *   workgroup, one per SIMD, for the register budget). d = 32 and 96 run on the 64 / 128
+ *   tiles but compute only their own width. Any other d runs on the next tile width up
+ *   with the extra columns zero-padded: zero columns add nothing to Q K^T, and the padded
+ *   output columns are never written. That costs the padded matrix work.
  *   scale must be finite and nonzero (negative values are allowed).
  *
  * Errors: every entry point validates its arguments on the host before any HIP call and

@@ -749,7 +749,7 @@ def test_fp8_long_ragged_length_sampled_rows():
     assert (vt[..., 16381:] == 0).all()
 
 
-# ------------------------------------------------------- head dims above 128 (forward)
+# ------------------------------------------------------------- head dims above 128
 
 @pytest.mark.parametrize("d", [256, 200])
 @pytest.mark.parametrize("N,causal,window,kv,bm", [
@@ -758,24 +758,32 @@ def test_fp8_long_ragged_length_sampled_rows():
     (300, False, (60, 20), None, None),
     (384, True, None, [384, 150], [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
 ])
-def test_forward_head_dims_above_128(d, N, causal, window, kv, bm):
+def test_head_dims_above_128(d, N, causal, window, kv, bm):
     B = 1 if kv is None else len(kv)
     q, k, v, do = inp.custom_inputs(B, 2, N, d, seed=173 + N + d)
     kvn = None if kv is None else np.array(kv, dtype=np.int32)
     bmn = None if bm is None else np.array(bm, dtype=np.uint8)
-    scale = float(np.float32(d ** -0.5))
-    say(f"[parity] forward d={d} N={N} causal={causal} window={window} kv={kv}")
-    res = Run(q, k, v, None, scale, causal, bmn, kvn, backward=False, window=window).result()
-    ref_o, ref_l = orc.forward(q, k, v, scale, causal, bmn, kvn, window=window)
-    check_o(res["O"], ref_o, f"d={d}")
-    check_lse(res["LSE"], ref_l, f"d={d}")
+    run_and_check(q, k, v, do, float(np.float32(d ** -0.5)), causal, bmn, kvn,
+                  what=f"head dim {d}", window=window)
 
 
-def test_forward_d200_is_bitwise_d256_on_zero_padded_tensors():
+def test_head_dim_256_f16_dropout():
+    N = 257
+    q, k, v, do = inp.custom_inputs(2, 2, N, 256, seed=181, dtype="f16")
+    kv = np.array([257, 100], dtype=np.int32)
+    drop = (0.15, 8888, 4)
+    say("[parity] head dim 256 f16 + dropout")
+    res = Run(q, k, v, do, 0.0625, True, None, kv, dropout=drop).result()
+    ref = orc.backward(q, k, v, do, 0.0625, True, None, kv, dropout=drop)
+    check_all(res, ref, "head dim 256 f16 dropout", o_rel_slack=DROP_O_SLACK)
+
+
+def test_d200_is_bitwise_d256_on_zero_padded_tensors():
     N = 300
-    q, k, v, _ = inp.custom_inputs(1, 2, N, 200, seed=179)
-    say("[bitexact] forward d=200 vs 256 zero-padded")
-    a = Run(q, k, v, None, 0.07, True, backward=False)
-    b = Run(*(_zero_pad_cols(x, 256) for x in (q, k, v)), None, 0.07, True, backward=False)
+    q, k, v, do = inp.custom_inputs(1, 2, N, 200, seed=179)
+    say("[bitexact] d=200 vs 256 zero-padded")
+    a = Run(q, k, v, do, 0.07, True)
+    b = Run(*(_zero_pad_cols(x, 256) for x in (q, k, v, do)), 0.07, True)
     assert _bits_equal(a.lse, b.lse)
-    assert _bits_equal(a.o, b.o[..., :200].contiguous())
+    for name in ("o", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)[..., :200].contiguous()), name
