@@ -76,25 +76,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // hardware overlap one wave's exponentials with the other's matrix products. K and V of
 // the tile stay in LDS (row-major, swizzled) for the whole pass.
 // D, DC, PAD as in the forward: LDS layout head dim, computed head dim, and whether the
-// head dim p.dh is below D. NW = 8: four key groups x two query halves, K and V tiles in
-// LDS. NW = 4 (d = 256, one wave per SIMD): four key groups x one query half of 32, and
-// each wave keeps its keys' K operands in registers, since a 256-wide K tile would not fit
-// in LDS beside the V tile and the query stages (K and V both in registers would spill).
+// head dim p.dh is below D. NW = 8: four key groups x two query halves of each 64-query
+// step; the halves add their dK, dV partials at the end. NW = 4 (d = 256, one wave per
+// SIMD): two key groups x two halves of the output columns, 32-query steps. Both waves of
+// a key group compute S and dP over the full d, and each accumulates dK, dV for its 128
+// columns: full-width accumulators (256 registers) would spill.
 template <typename T, int D, bool DROP, bool PAD, int DC, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr bool KREG = NW == 4;      // K operands in registers
-  constexpr int BKC = 128;            // keys per workgroup
+  constexpr bool CSPLIT = NW == 4;    // output columns split across waves
+  constexpr int BKC = CSPLIT ? 64 : 128;  // keys per workgroup
   constexpr int BQ = 8 * NW;          // queries per step (64, or 32 with NW = 4)
   constexpr int NS = DC / 16;         // contraction steps over d
-  constexpr int DB = DC / 32;         // 32-wide column blocks over d
+  constexpr int DB = (CSPLIT ? DC / 2 : DC) / 32;  // 32-wide output column blocks per wave
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;
   constexpr int QTILE = BQ * ROWB;    // bytes of one Q (or dO) tile
-  constexpr int VTILE = BKC * ROWB;   // bytes of the V tile
-  constexpr int KTILE = KREG ? 16 : VTILE;  // bytes of the K tile (none with KREG)
+  constexpr int KTILE = BKC * ROWB;   // bytes of the K (or V) tile
   constexpr int QLPW = QTILE / 1024 / NW;  // 1 KB DMA loads per wave per Q tile
-  constexpr int KLPW = VTILE / 1024 / NW;  // per wave for the K and V tiles
-  static_assert(KREG || (QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4),
+  constexpr int KLPW = KTILE / 1024 / NW;  // per wave for the K and V tiles
+  static_assert(CSPLIT || (QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4),
                 "dK/dV reduction space");
   // Every stage is its own array so the compiler can tell the tiles being read from the
   // ones being filled by in-flight copies, and does not wait for those before reading.
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(4096))) char sdO0[QTILE];
   __shared__ __attribute__((aligned(4096))) char sdO1[QTILE];
   __shared__ __attribute__((aligned(1024))) char sK[KTILE];
-  __shared__ __attribute__((aligned(1024))) char sV[VTILE];
+  __shared__ __attribute__((aligned(1024))) char sV[KTILE];
   // LSE and D of a step: 64 floats, what one wave-wide 4-byte copy writes.
   __shared__ __attribute__((aligned(256))) float sL0[64];
   __shared__ __attribute__((aligned(256))) float sL1[64];
@@ -119,8 +119,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int kg = wave & 3;                 // key group
-  const int qh = NW == 8 ? wave >> 2 : 0;  // query half of each step
+  const int kg = CSPLIT ? wave & 1 : wave & 3;  // key group
+  const int qh = CSPLIT ? 0 : wave >> 2;        // query half of each step
+  const int jo = CSPLIT ? (wave >> 1) * DB : 0;  // first output column block
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -190,21 +191,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     zero_pad<CH>(sQ1, QTILE, cha, tid, 64 * NW);
     zero_pad<CH>(sdO0, QTILE, cha, tid, 64 * NW);
     zero_pad<CH>(sdO1, QTILE, cha, tid, 64 * NW);
-    if constexpr (!KREG) zero_pad<CH>(sK, KTILE, cha, tid, 64 * NW);
-    zero_pad<CH>(sV, VTILE, cha, tid, 64 * NW);
-  }
-  // KREG: this lane's key row of K as the B operand of S (key kw + l%32, contraction
-  // slots 16k + 8hi .. +7 of step k); rows past klim load row klim-1 (masked).
-  typename T::vec8 kf[KREG ? NS : 1];
-  if constexpr (KREG) {
-    const int krow_g = min(mykey, max(klim, 1) - 1);
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (klim > 0 && (!PAD || 2 * k + hi < cha))
-        x = ldg16(K + (size_t)krow_g * ld + 16 * k + 8 * hi);
-      kf[k] = as_vec<T>(x);
-    }
+    zero_pad<CH>(sK, KTILE, cha, tid, 64 * NW);
+    zero_pad<CH>(sV, KTILE, cha, tid, 64 * NW);
   }
   int qt = next_q(qt_begin);
   if (qt < qt_end) {
@@ -217,7 +205,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
       const size_t goff = (size_t)min(k0 + row, klim - 1) * ld + lch * 8;
       if (!PAD || lch < cha) {
-        if constexpr (!KREG) g2lds16(K + goff, sK + g * 1024);
+        g2lds16(K + goff, sK + g * 1024);
         g2lds16(V + goff, sV + g * 1024);
       }
     }
@@ -267,11 +255,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
-      if constexpr (KREG)
-        s = mfma32(*reinterpret_cast<const typename T::vec8*>(Qs + ao), kf[k], s);
-      else
-        s = mfma32(*reinterpret_cast<const typename T::vec8*>(Qs + ao),
-                   *reinterpret_cast<const typename T::vec8*>(sK + bo), s);
+      s = mfma32(*reinterpret_cast<const typename T::vec8*>(Qs + ao),
+                 *reinterpret_cast<const typename T::vec8*>(sK + bo), s);
       dp = mfma32(*reinterpret_cast<const typename T::vec8*>(dOs + ao),
                   *reinterpret_cast<const typename T::vec8*>(sV + bo), dp);
       // Keep the scheduler from hoisting every operand load of the loop to its top.
@@ -324,13 +309,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       const int hoffb = half * 16 * ROWB;
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
-        const int o0 = hoffb + (t_off0 ^ (j << 6)), o1 = hoffb + (t_off1 ^ (j << 6));
+        const int jc = j + jo;  // column block of the d dimension
+        const int o0 = hoffb + (t_off0 ^ (jc << 6)), o1 = hoffb + (t_off1 ^ (jc << 6));
         acc_dv[j] = mfma32(pa, cat_tr<T>(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
         acc_dk[j] = mfma32(da, cat_tr<T>(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
-        // d = 256: keep the operand loads of all eight column blocks from being hoisted at
-        // once (the accumulators already hold 256 registers).
-        if constexpr (KREG)
-          if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -361,14 +343,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     qt = qc;
   }
 
-  if constexpr (KREG) {  // one query half: store directly. dK = scale * (dS^T Q), dV = P^T dO.
+  if constexpr (CSPLIT) {  // one query half: store directly. dK = scale * dS^T Q, dV = P^T dO.
 #pragma unroll
     for (int j = 0; j < DB; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kw + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (key < N && (!PAD || j * 32 + l32 < ld)) {
-          const size_t off = hoff + (size_t)key * ld + j * 32 + l32;
+        const int col = (j + jo) * 32 + l32;
+        if (key < N && (!PAD || col < ld)) {
+          const size_t off = hoff + (size_t)key * ld + col;
           p.dk[off] = (uint16_t)T::bits(acc_dk[j][i] * p.scale);
           p.dv[off] = (uint16_t)T::bits(acc_dv[j][i]);
         }
@@ -664,10 +647,10 @@ hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh);
-  if (d > 128) {  // 256-wide tiles, four waves (dQ: 128 queries per workgroup)
-    const dim3 g_q4((unsigned)((p.N + 127) / 128) * bh);
-    if (d == 256) return launch_main<T, 256, DROP, false, 256, 4>(p, g_kv, g_q4, stream);
-    return launch_main<T, 256, DROP, true, 256, 4>(p, g_kv, g_q4, stream);
+  if (d > 128) {  // 256-wide tiles, four waves: dK/dV 64 keys, dQ 128 queries per workgroup
+    const dim3 g_kv4((unsigned)((p.N + 63) / 64) * bh), g_q4((unsigned)((p.N + 127) / 128) * bh);
+    if (d == 256) return launch_main<T, 256, DROP, false, 256, 4>(p, g_kv4, g_q4, stream);
+    return launch_main<T, 256, DROP, true, 256, 4>(p, g_kv4, g_q4, stream);
   }
   const dim3 g_q((unsigned)((p.N + 255) / 256) * bh);
   // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
