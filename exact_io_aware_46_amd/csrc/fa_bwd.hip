@@ -17,10 +17,11 @@
 // query-outer pass recomputes S and dP per tile and accumulates dQ in registers (three
 // MFMA products instead of one, no atomics, and dQ is deterministic).
 //
-// gfx950 mapping shared by both passes: 4 waves per workgroup, each owning 32 rows of
-// the outer dimension; inner tiles are copied HBM -> LDS by global_load_lds (no
-// registers), double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that
-// must be contraction-major are read with LDS transpose loads.
+// gfx950 mapping shared by both passes: 8 waves per workgroup (two per SIMD; 4 at d = 256,
+// where the accumulators need one wave per SIMD), each owning 32 rows of the outer
+// dimension; inner tiles are copied HBM -> LDS by global_load_lds (no registers),
+// double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that must be
+// contraction-major are read with LDS transpose loads.
 #include <type_traits>
 
 #include "fa_device.hpp"

@@ -14,7 +14,8 @@
 //
 // gfx950 mapping:
 //   workgroup = 8 waves = 256 queries of one (b, h); wave w owns queries 32w .. 32w+31
-//   (two waves per SIMD, and every K/V tile copied into LDS serves 256 queries).
+//   (two waves per SIMD, and every K/V tile copied into LDS serves 256 queries). At
+//   d = 256 the O accumulators need one wave per SIMD: 4 waves = 128 queries.
 //   Key tiles (BC keys) of K and V are copied HBM -> LDS by the DMA path of the vector
 //   memory unit (global_load_lds, no registers), double-buffered so the next tile streams
 //   in while the current one is used, and kept row-major with XOR-swizzled 16-byte chunks.
