@@ -421,12 +421,13 @@ def main():
     # Kernel template names as the profiler prints them.
     tn = "fa::F16" if wl.dtype == "f16" else "fa::Bf16"
     dr = "true" if wl.dropout is not None and wl.dropout[0] > 0 else "false"
-    kd = 128 if wl.d > 64 else 64                              # kernel (LDS layout) head dim
+    kd = 256 if wl.d > 128 else 128 if wl.d > 64 else 64      # kernel (LDS layout) head dim
     pad = "false" if wl.d == kd else "true"                    # rows narrower than kd
     dc = wl.d if wl.d in (32, 96) else kd                      # head dim computed on
-    k_dkdv = f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>"
-    k_dq = f"bwd_dq_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}>"
-    k_fwd = f"fwd_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}>"
+    nw = 4 if kd == 256 else 8                                 # waves per workgroup
+    k_dkdv = f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>"
+    k_dq = f"bwd_dq_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}, {nw}>"
+    k_fwd = f"fwd_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}, {nw}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -98,8 +98,8 @@ class Workload:
 # The workloads, in order: a tiny single head, a GPT-2-small-shaped causal layer, a
 # BERT-large-shaped padded layer, a long causal head set, a block-sparse layer, the long
 # head set with a sliding window, the long causal head set in fp16, the long causal head
-# set with attention dropout, the long causal head set at head dims 96 and 32, and the long
-# causal head set in FP8.
+# set with attention dropout, the long causal head set at head dims 96, 32 and 256, and the
+# long causal head set in FP8.
 WORKLOADS = {
     "single_head_256": Workload("single_head_256", 1, 1, 256, 64, seed=46001),
     "gpt2s_causal_1k": Workload("gpt2s_causal_1k", 8, 12, 1024, 64, causal=True, seed=46002),
@@ -126,6 +126,8 @@ WORKLOADS = {
                                     seed=46009),
     "long_causal_16k_d32": Workload("long_causal_16k_d32", 1, 16, 16384, 32, causal=True,
                                     seed=46010),
+    "long_causal_16k_d256": Workload("long_causal_16k_d256", 1, 16, 16384, 256, causal=True,
+                                     seed=46012),
     # The long causal head set in FP8 (E4M3 with per-tensor descales; forward only).
     "long_causal_16k_fp8": Workload("long_causal_16k_fp8", 1, 16, 16384, 128, causal=True,
                                     seed=46011, dtype="fp8"),

@@ -237,7 +237,8 @@ def test_workload_full_compare(name):
 
 @pytest.mark.parametrize("name", ["long_causal_16k", "blocksparse_8k", "sliding_window_16k",
                                   "long_causal_16k_f16", "long_causal_16k_dropout",
-                                  "long_causal_16k_d96", "long_causal_16k_d32"])
+                                  "long_causal_16k_d96", "long_causal_16k_d32",
+                                  "long_causal_16k_d256"])
 def test_workload_sampled_compare(name):
     wl = inp.WORKLOADS[name]
     x = inp.make_inputs(wl)
