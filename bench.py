@@ -427,7 +427,8 @@ def main():
     nw = 4 if kd == 256 else 8                                 # waves per workgroup
     k_dkdv = f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>"
     k_dq = f"bwd_dq_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}, {nw}>"
-    k_fwd = f"fwd_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}, {nw}>"
+    bc = 128 if kd == 128 else 64                              # forward key tile
+    k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nw}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -16,9 +16,10 @@
 //   workgroup = 8 waves = 256 queries of one (b, h); wave w owns queries 32w .. 32w+31
 //   (two waves per SIMD, and every K/V tile copied into LDS serves 256 queries). At
 //   d = 256 the O accumulators need one wave per SIMD: 4 waves = 128 queries.
-//   Key tiles (BC keys) of K and V are copied HBM -> LDS by the DMA path of the vector
-//   memory unit (global_load_lds, no registers), double-buffered so the next tile streams
-//   in while the current one is used, and kept row-major with XOR-swizzled 16-byte chunks.
+//   Key tiles (BC keys: 128 on the 128-wide layout, 64 on the others) of K and V are copied
+//   HBM -> LDS by the DMA path of the vector memory unit (global_load_lds, no registers),
+//   double-buffered so the next tile streams in while the current one is used (128 KB of
+//   LDS at d = 128), and kept row-major with XOR-swizzled 16-byte chunks.
 //   The score tile is computed transposed, S^T = K Q^T, with MFMA 32x32x16 (bf16 -> fp32):
 //   lane l then holds scores of query (l % 32) only, so the row maximum is an in-lane
 //   reduction plus one cross-half permlane swap, and the exponentiated tile is already in
@@ -47,6 +48,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   constexpr int ROWB = D * 2;       // bytes per row
   constexpr int TILE = BC * ROWB;   // bytes of one K (or V) tile
   constexpr int LPW = TILE / 1024 / NW;  // 1 KB wave-wide DMA loads per wave per tile
+  constexpr int QPF = 2;  // score MFMA steps the K operand reads run ahead
+  constexpr int VPF = 3;  // P V MFMAs the V^T reads run ahead
   // Two stages (double buffering) of a K tile and a V tile, both row-major, swizzled.
   // Each stage is its own array so the compiler can tell the tile being read from the one
   // being filled and does not wait for the in-flight copy before reading.
@@ -173,13 +176,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
 
     f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = zero16();
+    for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
+    // Contraction step outer, key block inner: consecutive MFMAs are independent.
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
         s[kb] = mfma32(*reinterpret_cast<const typename T::vec8*>(
                            sK + kb * 32 * ROWB + (k_off ^ (st << 5))),
                        qf[st], s[kb]);
+    // Issue order: the K operands of the first QPF steps, then each step's MFMAs followed
+    // by the reads of the step QPF ahead, so no MFMA waits on a just-issued LDS read.
+    __builtin_amdgcn_sched_group_barrier(0x100, KB * QPF, 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
+      if (st + QPF < NS) __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
     }
 
     if (k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim) {
@@ -251,6 +263,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
           acc[j] = mfma32(vf, pf, acc[j]);
         }
       }
+    // Same for the P V product: the V^T reads (two per MFMA) run VPF MFMAs ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+    for (int m = 0; m < KB * 2 * DB; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m + VPF < KB * 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
   // Main loop, unrolled twice so each half reads one fixed stage while the other fills.
@@ -307,13 +326,15 @@ hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
   }
   const dim3 grid((unsigned)((p.N + 255) / 256) * bh);
   // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
-  // head dims run the next kernel up on zero-padded tiles.
+  // head dims run the next kernel up on zero-padded tiles. The 128 layout takes key tiles
+  // of 128 (one barrier, one copy round and one row-maximum reduction per 128 keys); the
+  // 64 layout's registers and the 256 layout's LDS hold tiles of 64.
   if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, false, 128, 8>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, false, 128, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 96)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
   else if (d > 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 64, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 64)
     hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 32)

@@ -295,13 +295,14 @@ def test_sliding_window(d, N, causal, window, kv, bm):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_keys_outside_every_window_are_bitwise_invisible(d):
-    """Window (64, 0): rows >= 256 see only keys >= 192, so NaN in keys and values below
-    192 must leave those rows bitwise unchanged (the tiles are never read)."""
+    """Window (64, 0): rows >= 256 see only keys >= 192, so NaN in the keys and values
+    below 128 (whole key tiles below every such row's window, for tiles of 64 or 128 keys)
+    must leave those rows bitwise unchanged (the tiles are never read)."""
     N = 512
     q, k, v, do = inp.custom_inputs(1, 2, N, d, seed=67)
     kp, vp = k.copy(), v.copy()
-    kp[:, :, :192] = 0x7FC0
-    vp[:, :, :192] = 0x7FC0
+    kp[:, :, :128] = 0x7FC0
+    vp[:, :, :128] = 0x7FC0
     say(f"[bitexact] window poison d={d}")
     a = Run(q, k, v, None, 0.125, False, backward=False, window=(64, 0))
     b = Run(q, kp, vp, None, 0.125, False, backward=False, window=(64, 0))
