@@ -95,6 +95,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KTILE = BKC * ROWB;   // bytes of the K (or V) tile
   constexpr int QLPW = QTILE / 1024 / NW;  // 1 KB DMA loads per wave per Q tile
   constexpr int KLPW = KTILE / 1024 / NW;  // per wave for the K and V tiles
+  constexpr int PF = 2;  // S / dP steps the operand reads run ahead (one wave per SIMD)
+  constexpr int VPF = 2;  // dV, dK MFMA pairs the transpose reads run ahead (same)
   static_assert(CSPLIT || (QTILE >= 32 * D * 4 && KTILE / 2 >= 32 * D * 4),
                 "dK/dV reduction space");
   // Every stage is its own array so the compiler can tell the tiles being read from the
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
     if constexpr (DROP) dp = zero16();
     else dp = nd;
+    if constexpr (NW == 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int ao = a_off ^ (k << 5), bo = b_off ^ (k << 5);
@@ -260,8 +263,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
                  *reinterpret_cast<const typename T::vec8*>(sK + bo), s);
       dp = mfma32(*reinterpret_cast<const typename T::vec8*>(dOs + ao),
                   *reinterpret_cast<const typename T::vec8*>(sV + bo), dp);
-      // Keep the scheduler from hoisting every operand load of the loop to its top.
-      if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      // Two waves per SIMD: keep the scheduler from hoisting every operand load of the
+      // loop to its top (the other wave covers the read latency).
+      if (NW == 8 && k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NW == 4) {
+      // One wave per SIMD: nothing else covers the LDS latency, so the reads of step k + PF
+      // are issued right after the two MFMAs of step k.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PF, 0);
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (k + PF < NS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Dropout draws of this lane's key for its 16 queries (element i is query
     // q0 + 32*qh + 16*(i/8) + 8*hi + i%8). The quad of lanes holding keys 4*(mykey/4) .. +3
@@ -314,6 +329,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
         const int o0 = hoffb + (t_off0 ^ (jc << 6)), o1 = hoffb + (t_off1 ^ (jc << 6));
         acc_dv[j] = mfma32(pa, cat_tr<T>(lds_tr4(dOs + o0), lds_tr4(dOs + o1)), acc_dv[j]);
         acc_dk[j] = mfma32(da, cat_tr<T>(lds_tr4(Qs + o0), lds_tr4(Qs + o1)), acc_dk[j]);
+      }
+    }
+    if constexpr (NW == 4) {
+      // The dO^T and Q^T transpose reads (four per dV, dK pair) run VPF pairs ahead; the
+      // first group also takes the LSE reads of the first half.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + 4 * VPF, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * DB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (m + VPF < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
     }
   };
@@ -408,6 +433,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
   constexpr int LPW = TILE / 1024 / NW;  // 1 KB DMA loads per wave per tile
+  constexpr int PF = 2;   // S / dP steps the K and V reads run ahead
+  constexpr int VPF = 3;  // dQ MFMAs the K^T transpose reads run ahead
   __shared__ __attribute__((aligned(1024))) char sK0[TILE];
   __shared__ __attribute__((aligned(1024))) char sV0[TILE];
   __shared__ __attribute__((aligned(1024))) char sK1[TILE];
@@ -537,7 +564,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
         const int off = kbo + (a_off ^ (st << 5));
         s = mfma32(*reinterpret_cast<const typename T::vec8*>(sK + off), qf[st], s);
         dp = mfma32(*reinterpret_cast<const typename T::vec8*>(sV + off), gf[st], dp);
-        if (st % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      // Issue order: the K and V reads run PF steps ahead of their two MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (st + PF < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       // Dropout draws: element i is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8.
       uint32_t kwd[DROP ? 8 : 1];
@@ -567,6 +600,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
           const typename T::vec8 kf = cat_tr<T>(lds_tr4(sK + o0), lds_tr4(sK + o1));
           acc[j] = mfma32(kf, df, acc[j]);
         }
+      }
+      // The K^T transpose reads (two per MFMA) run VPF MFMAs ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * DB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m + VPF < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
   };
