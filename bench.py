@@ -426,8 +426,8 @@ def main():
     dc = wl.d if wl.d in (32, 96) else kd                      # head dim computed on
     nw = 4 if kd == 256 else 8                                 # waves per workgroup
     k_dkdv = f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>"
-    k_dq = f"bwd_dq_kernel<{tn}, {kd}, 64, {dr}, {pad}, {dc}, {nw}>"
-    bc = 128 if kd == 128 else 64                              # forward key tile
+    bc = 128 if kd == 128 else 64                              # forward and dQ key tile
+    k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nw}>"
     k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nw}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -676,7 +676,11 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
                      p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, 64, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
+  // The dQ pass keeps one 32-key block of S and dP live at a time, so on the 128 layout
+  // its key tiles can hold 128 keys (one barrier and copy round per 128 keys; 128 KB of
+  // LDS); the 64 and 256 layouts take tiles of 64.
+  constexpr int BCQ = D == 128 ? 128 : 64;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
                      stream, p);
   return hipGetLastError();
 }
