@@ -233,21 +233,27 @@ def fp8_main(args, torch, wl, x):
 
 
 def device_sample(torch, fn, seconds=5.0):
-    """Clock and power while the GPU runs ``fn`` back to back: about 0.5 s of steps are
-    queued first (so the clocks have ramped), then one ``amd-smi metric`` query runs in a
-    child process while steps keep the queue full. Returns None if amd-smi is missing or
-    fails."""
+    """Clock and power while the GPU runs ``fn`` back to back: about 1 s of steps runs
+    first (so the clocks have ramped), then one ``amd-smi metric`` query runs in a child
+    process while steps keep the queue full (synchronising every ~100 ms of work). A
+    reading below 1 GHz means the query caught the GPU idle and is labelled as such.
+    Returns None if amd-smi is missing or fails."""
     import shutil
     import subprocess
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    chunk = max(20, int(0.1 / max(time.perf_counter() - t0, 1e-5)))  # steps per ~100 ms
     n = 0
-    while time.perf_counter() - t0 < 0.5:
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
         fn()
         n += 1
-        if n % 20 == 0:
+        if n % chunk == 0:
             torch.cuda.synchronize()
     try:
         proc = subprocess.Popen([exe, "metric", "-c", "-p", "--json"], stdout=subprocess.PIPE,
@@ -259,7 +265,7 @@ def device_sample(torch, fn, seconds=5.0):
     while proc.poll() is None and time.perf_counter() - t1 < seconds:
         fn()
         n += 1
-        if n % 20 == 0:
+        if n % chunk == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     try:
@@ -267,9 +273,12 @@ def device_sample(torch, fn, seconds=5.0):
         gpu = json.loads(out)["gpu_data"][0]
         clks = [v["clk"]["value"] for k, v in gpu["clock"].items()
                 if k.startswith("gfx_") and isinstance(v, dict) and "clk" in v]
-        return {"gfx_clk_mhz_mean": round(sum(clks) / len(clks), 1), "gfx_clk_mhz": clks,
-                "socket_power_w": gpu["power"]["socket_power"]["value"],
-                "source": "amd-smi metric -c -p, sampled while steps ran"}
+        rec = {"gfx_clk_mhz_mean": round(sum(clks) / len(clks), 1), "gfx_clk_mhz": clks,
+               "socket_power_w": gpu["power"]["socket_power"]["value"],
+               "source": "amd-smi metric -c -p, sampled while steps ran"}
+        if rec["gfx_clk_mhz_mean"] < 1000:
+            rec["note"] = "below 1 GHz: the query caught the GPU idle; not the clock under load"
+        return rec
     except Exception:  # noqa: BLE001 -- the sample is optional context
         proc.kill()
         return None
