@@ -164,9 +164,27 @@ __device__ __forceinline__ void zero_pad(char* tile, int bytes, int valid, int t
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
 }
-// Same with 4 bytes per lane: lane l's word lands at lds_base + 4 * l.
-__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 4, 0, 0);
+
+// The same copies through a buffer resource. The compiler's wait-count pass takes a global
+// LDS-DMA load for a flat access that may also touch LDS: while one is in flight it waits
+// for every outstanding LDS read (lgkmcnt(0)) before any use of LDS data, which undoes the
+// operand reads issued ahead of their matrix instructions. Buffer loads do not count as
+// flat, so the waits stay partial. buf_rsrc describes `bytes` bytes from `base` (raw, no
+// stride; word 3 selects the 32-bit data format that untyped buffer loads need on this
+// family); a load past `bytes` returns zeros. Each copy builds its resource at the first
+// row of its tile, so offsets stay small whatever the tensor size.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           0x00020000);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// Lane l's 16 (4) bytes at byte `off` of the resource land at lds_base + 16 l (4 l).
+__device__ __forceinline__ void buf2lds16(rsrc_t r, int off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void buf2lds4(rsrc_t r, int off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -113,16 +113,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   // and reading a valid row keeps every access in bounds).
   auto issue = [&](int kt, char* dK, char* dV) {
     const int k0 = kt * BC;
+    const rsrc_t rk = buf_rsrc(K + (size_t)k0 * ld, BC * ld * 2);
+    const rsrc_t rv = buf_rsrc(V + (size_t)k0 * ld, BC * ld * 2);
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
       const int g = wave * LPW + t;
       const int byte = g * 1024 + lane * 16;
       const int row = byte / ROWB;
       const int lch = ((byte % ROWB) >> 4) ^ swz<CH>(row);
-      const size_t goff = (size_t)min(k0 + row, klim - 1) * ld + lch * 8;
+      const int toff = (min(k0 + row, klim - 1) - k0) * ld * 2 + lch * 16;
       if (!PAD || lch < cha) {
-        g2lds16(K + goff, dK + g * 1024);
-        g2lds16(V + goff, dV + g * 1024);
+        buf2lds16(rk, toff, dK + g * 1024);
+        buf2lds16(rv, toff, dV + g * 1024);
       }
     }
   };
