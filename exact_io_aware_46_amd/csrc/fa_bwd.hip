@@ -18,8 +18,8 @@
 // MFMA products instead of one, no atomics, and dQ is deterministic).
 //
 // gfx950 mapping shared by both passes: 8 waves per workgroup (two per SIMD; 4 at d = 256,
-// where the accumulators need one wave per SIMD), each owning 32 rows of the outer
-// dimension; inner tiles are copied HBM -> LDS by global_load_lds (no registers),
+// where the accumulators need one wave per SIMD, and 4 in the dK/dV pass on the 128-wide
+// layout, which keeps K and V in registers), each owning 32 rows of the outer dimension; inner tiles are copied HBM -> LDS by global_load_lds (no registers),
 // double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that must be
 // contraction-major are read with LDS transpose loads.
 #include <type_traits>
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------- dK, dV pass, one wave per SIMD (d <= 128)
+// ------------------------------- dK, dV pass, one wave per SIMD (128-wide layout)
 
 // Workgroup = 4 waves = 128 keys of one (b, h); wave w owns keys 32w .. 32w+31 and every
 // query of each 64-query step, as two 32-query blocks. At one wave per SIMD a lane has 512
@@ -997,7 +997,13 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
 
 template <typename T, int D, bool DROP, bool PAD, int DC, int NW = 8>
 hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
-  if constexpr (NW == 8)  // d <= 128: one wave per SIMD, K and V in registers
+  // 128-wide layout (head dims 65 .. 128): one wave per SIMD with K and V in registers,
+  // 1.5% faster than the two-wave kernel at d = 128. d = 96 runs it too, although 0.8%
+  // slower there, so that every head dim of the layout sums in the order of d = 128 (its
+  // results equal those of d = 128 on zero-padded tensors bit for bit). On the 64-wide
+  // layout a step holds too little matrix work to cover one wave's exponentials, and the
+  // two-wave kernel is 3-10% faster.
+  if constexpr (NW == 8 && D == 128)
     hipLaunchKernelGGL((bwd_dkdv_rk_kernel<T, D, DROP, PAD, DC>), g_kv, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC, NW>), g_kv, dim3(64 * NW), 0,

@@ -159,13 +159,10 @@ __device__ __forceinline__ void zero_pad(char* tile, int bytes, int valid, int t
   }
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 * l (lds_base must be the same for the whole wave).
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
-}
 
-// The same copies through a buffer resource. The compiler's wait-count pass takes a global
+// Direct global -> LDS copies (no registers involved) through a buffer resource: lane l's
+// bytes land at lds_base + size * l (lds_base must be the same for the whole wave). They
+// are buffer rather than global loads because the compiler's wait-count pass takes a global
 // LDS-DMA load for a flat access that may also touch LDS: while one is in flight it waits
 // for every outstanding LDS read (lgkmcnt(0)) before any use of LDS data, which undoes the
 // operand reads issued ahead of their matrix instructions. Buffer loads do not count as

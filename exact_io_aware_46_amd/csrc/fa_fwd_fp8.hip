@@ -145,16 +145,22 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   };
   // Key tile kt -> stage: K rows (rows at or past klim fetch row klim-1, masked later) and
   // the V^T columns k0 .. k0+63 (zero past N in the workspace).
+  // Both copies go through buffer resources based at the tile (see buf_rsrc). The V^T
+  // tile spans D rows of the transposed workspace: its offsets, below D * Np <= N * d +
+  // 63 d, stay under 2^32 because the C ABI keeps N * d below 2^31 (offsets and sizes are
+  // passed as their unsigned 32-bit patterns).
   auto issue = [&](int kt, char* dK, char* dV) {
     const int k0 = kt * BC;
+    const rsrc_t rk = buf_rsrc(K + (size_t)k0 * D, KT);
+    const rsrc_t rv = buf_rsrc(Vt + k0, (int)((uint32_t)(D - 1) * (uint32_t)p.Np + BC));
     for (int g = wave; g < KLOADS; g += 8) {
       const int byte = g * 1024 + lane * 16;
       const int krow = byte / D;
       const int kch = ((byte % D) >> 4) ^ swz_k8<D>(krow);
-      g2lds16(K + (size_t)min(k0 + krow, klim - 1) * D + kch * 16, dK + g * 1024);
+      buf2lds16(rk, (min(k0 + krow, klim - 1) - k0) * D + kch * 16, dK + g * 1024);
       const int vrow = byte >> 6;
       const int vch = ((byte & 63) >> 4) ^ swz_v8(vrow);
-      g2lds16(Vt + (size_t)vrow * p.Np + k0 + vch * 16, dV + g * 1024);
+      buf2lds16(rv, (int)((uint32_t)vrow * (uint32_t)p.Np + vch * 16), dV + g * 1024);
     }
   };
 
