@@ -17,7 +17,7 @@
 //   (two waves per SIMD, and every K/V tile copied into LDS serves 256 queries). At
 //   d = 256 the O accumulators need one wave per SIMD: 4 waves = 128 queries.
 //   Key tiles (BC keys: 128 on the 128-wide layout, 64 on the others) of K and V are copied
-//   HBM -> LDS by the DMA path of the vector memory unit (global_load_lds, no registers),
+//   HBM -> LDS by the DMA path of the vector memory unit (buffer loads into LDS, no registers),
 //   double-buffered so the next tile streams in while the current one is used (128 KB of
 //   LDS at d = 128), and kept row-major with XOR-swizzled 16-byte chunks.
 //   The score tile is computed transposed, S^T = K Q^T, with MFMA 32x32x16 (bf16 -> fp32):
