@@ -771,7 +771,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // The wave index is uniform across the wave: readfirstlane tells the compiler so, which
+  // makes every per-wave tile test a scalar branch (a divergent one it would if-convert,
+  // running the masked instance of the tile body on every tile).
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -875,11 +878,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   // One key tile: S^T and dP^T (lane l holds query l%32), P and dS in fp32, then
   // dQ^T += K^T dS^T with dS^T as the B operand straight from registers and K^T read from
   // the row-major K tile by transpose loads.
-  auto compute = [&](int kt, const char* sK, const char* sV) {
-    const int k0 = kt * BC;
-    if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
-    if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
-    const bool need_mask = k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim;
+  // Tiles that need no element mask use an instance without any mask code: a mask test
+  // inside the element loop compiles to one divergent branch per element, which splits the
+  // loop into blocks the scheduler cannot interleave with the matrix instructions.
+  auto tile = [&](auto masked, int k0, const char* sK, const char* sV, bool need_mask)
+                  __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     // One 32-key block at a time, so only one block of S and dP is live.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -901,14 +905,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
       // Dropout draws: element i is key k0 + 32*kb + 16*(i/8) + 8*hi + i%8.
       uint32_t kwd[DROP ? 8 : 1];
       if constexpr (DROP) drop_words_query_lane(kwd, k0 + kb * 32 + 8 * hi, myq, dk);
+      // Exponent of P; a masked element's is -inf (P = 0 for either sign of the scale).
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = s[i] * sc - lq;
+      if (MASKED && need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + acc_row(i, hi);
+          const bool ok = (key < klim) & (key <= myq + rl) & (key >= myq - ll);
+          s[i] = ok ? s[i] : -kInf;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(s[i] * sc - lq);
-        if (need_mask) {
-          const int key = k0 + kb * 32 + acc_row(i, hi);
-          const bool ok = key < klim && key <= myq + rl && key >= myq - ll;
-          if (!ok) pv = 0.f;
-        }
+        const float pv = fast_exp2(s[i]);
         if constexpr (DROP) {
           const bool keep = drop_keep(kwd[i >> 1], i & 1, p.drop_t, thi);
           dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + ndq);  // dS = P (dP - D)
@@ -934,6 +944,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (m + VPF < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+    }
+  };
+  auto compute = [&](int kt, const char* sK, const char* sV) {
+    const int k0 = kt * BC;
+    if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
+    if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
+    const bool need_mask = k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim;
+    if constexpr (D == 64) {
+      if (need_mask) tile(std::true_type{}, k0, sK, sV, true);
+      else tile(std::false_type{}, k0, sK, sV, false);
+    } else {  // two inlined instances of the wider tiles exceed the register budget
+      tile(std::true_type{}, k0, sK, sV, need_mask);
     }
   };
 
