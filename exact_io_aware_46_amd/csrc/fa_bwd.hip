@@ -311,12 +311,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * half + j;
-        float pv = fast_exp2(s[i] * sc - lv[j]);
+        // A masked element's exponent is -inf (P = 0 for either sign of the scale); masking
+        // the exponential's result instead lets the compiler branch around it per element.
+        float arg = s[i] * sc - lv[j];
         if constexpr (MASKED) {
           const int q = q0 + qloc + j;
-          const bool ok = mykey < klim && mykey <= q + rl && mykey >= q - ll && q < N;
-          pv = ok ? pv : 0.f;
+          const bool ok = (mykey < klim) & (mykey <= q + rl) & (mykey >= q - ll) & (q < N);
+          arg = ok ? arg : -kInf;
         }
+        const float pv = fast_exp2(arg);
         if constexpr (DROP) {
           const bool keep = drop_keep(kwd[i >> 1], i & 1, p.drop_t, thi);
           s[i] = keep ? pv * p.drop_rp : 0.f;                    // P_drop, for dV
@@ -620,12 +623,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
           }
         }
       }
-      float pv = fast_exp2(s[h][i] * sc - lv[h][i]);
+      // A masked element's exponent is -inf (P = 0 for either sign of the scale).
+      float arg = s[h][i] * sc - lv[h][i];
       if constexpr (MASKED) {
         const int q = q0 + 32 * h + acc_row(i, hi);
-        const bool ok = mykey < klim && mykey <= q + rl && mykey >= q - ll && q < N;
-        pv = ok ? pv : 0.f;
+        const bool ok = (mykey < klim) & (mykey <= q + rl) & (mykey >= q - ll) & (q < N);
+        arg = ok ? arg : -kInf;
       }
+      const float pv = fast_exp2(arg);
       if constexpr (DROP) {
         const bool keep = drop_keep(kwd[h][i >> 1], i & 1, p.drop_t, thi);
         s[h][i] = keep ? pv * p.drop_rp : 0.f;
