@@ -432,41 +432,40 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------- dK, dV pass, one wave per SIMD (128-wide layout)
 
 // Workgroup = 4 waves = 128 keys of one (b, h); wave w owns keys 32w .. 32w+31 and every
-// query of each 128-query step, as four 32-query blocks. At one wave per SIMD a lane has
-// 512 registers, enough to keep the wave's K and V rows in registers as the B operands of
+// query of each 64-query step, as two 32-query blocks. At one wave per SIMD a lane has 512
+// registers, enough to keep the wave's K and V rows in registers as the B operands of
 // S = Q K^T and dP = dO V^T for the whole pass: per step only the Q and dO tiles are read
 // from LDS, once as row operands and once by transpose loads, a third of the LDS bytes per
 // product of the two-wave kernel. With no second wave on the SIMD to cover the softmax,
-// the wave overlaps it with its own matrix products, as a pipeline over the blocks of a
-// step (PipeOps): phase f issues the S, dP products of block f and the dV, dK products of
-// block f-2, and beside them the elementwise work (P, dS) of block f-1, one element per
-// one or two matrix instructions. The order is pinned with sched_barrier fences, and the
-// LDS operand reads run a few matrix instructions ahead of their use. Only the first and
-// last phase of a step have no elementwise work beside them. The waves own disjoint keys
-// and all columns, so dK and dV are stored with no reduction between waves.
+// the wave overlaps it with its own matrix products: the instruction stream of a step is
+// pinned (sched_barrier fences) as
+//   S, dP of block 0 | S, dP of block 1 + P, dS of block 0 | dV, dK of block 0 + P, dS of
+//   block 1 | dV, dK of block 1,
+// one or two elementwise elements per matrix instruction, with the LDS operand reads
+// issued a few matrix instructions ahead of their use. The waves own disjoint keys and all
+// columns, so dK and dV are stored with no reduction between waves.
 template <typename T, int D, bool DROP, bool PAD, int DC>
 __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
-  constexpr int BQ = 128;             // queries per step (one LDS stage)
-  constexpr int NB = BQ / 32;         // 32-query blocks per step
+  constexpr int BQ = 64;              // queries per step
   constexpr int NS = DC / 16;         // contraction steps over d
   constexpr int DB = DC / 32;         // 32-wide output column blocks
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
   constexpr int QTILE = BQ * ROWB;
   constexpr int QLPW = QTILE / 1024 / 4;  // 1 KB DMA loads per wave per Q (dO) tile
-  constexpr int NU = 4 * DB;              // dV, dK products per block (= its S, dP count)
-  using Ops = PipeOps<NB, 2 * NS, NU>;
-  constexpr int NOPS = Ops::total();
-  constexpr int LA = 3;                   // matrix instructions the operand reads run ahead
+  constexpr int NP = 2 * NS;              // S, dP contraction slots of a step (two blocks)
+  constexpr int NU = 4 * DB;              // dV, dK products per block
+  constexpr int PF = 2;                   // slots the row-operand reads run ahead
+  constexpr int VPF = 3;                  // products the transpose reads run ahead
   __shared__ __attribute__((aligned(4096))) char sQ0[QTILE];
   __shared__ __attribute__((aligned(4096))) char sQ1[QTILE];
   __shared__ __attribute__((aligned(4096))) char sdO0[QTILE];
   __shared__ __attribute__((aligned(4096))) char sdO1[QTILE];
-  __shared__ __attribute__((aligned(512))) float sL0[BQ];
-  __shared__ __attribute__((aligned(512))) float sL1[BQ];
-  __shared__ __attribute__((aligned(512))) float sD0[BQ];
-  __shared__ __attribute__((aligned(512))) float sD1[BQ];
+  __shared__ __attribute__((aligned(256))) float sL0[64];
+  __shared__ __attribute__((aligned(256))) float sL1[64];
+  __shared__ __attribute__((aligned(256))) float sD0[64];
+  __shared__ __attribute__((aligned(256))) float sD1[64];
 
   const int N = p.N;
   const int BH = p.B * p.H;
@@ -529,11 +528,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
         buf2lds16(rg, toff, ddO + g * 1024);
       }
     }
-    // LSE and D of the step's queries: one wave-wide 4-byte copy per 64 of them.
-    const int lrow = 64 * (wave & 1) + lane;
-    const int loff = (min(q0 + lrow, N - 1) - q0) * 4;
-    if (wave < 2) buf2lds4(buf_rsrc(L2 + q0, BQ * 4), loff, dL + 64 * (wave & 1));
-    else buf2lds4(buf_rsrc(DL + q0, BQ * 4), loff, dD + 64 * (wave & 1));
+    const int loff = (min(q0 + lane, N - 1) - q0) * 4;
+    if (wave == 0) buf2lds4(buf_rsrc(L2 + q0, 64 * 4), loff, dL);
+    if (wave == 1) buf2lds4(buf_rsrc(DL + q0, 64 * 4), loff, dD);
   };
 
   if constexpr (PAD && DC == D) {
@@ -580,45 +577,40 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
     constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qt * BQ;
     // Accumulator element i of block h in lane half hi is query q0 + 32h + acc_row(i, hi).
-    f32x16 s[NB], dp[NB], nd[NB];
-    float lv[NB][16];
-    uint32_t kwd[NB][DROP ? 8 : 1];
-    typename T::vec8 pa[NB][2], da[NB][2];  // [block][half] P and dS as A operands
-
-    // -D of block h's queries; dP starts there (the products add dO V^T). With dropout the
-    // product must be masked and scaled first, so it starts at 0 and -D is added later.
-    auto load_nd = [&](int h) __attribute__((always_inline)) {
+    f32x16 s[2], dp[2], nd[2];
+    float lv[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int qloc = 32 * h + 16 * half + 8 * hi;
         const float4 ga = *reinterpret_cast<const float4*>(&Ds[qloc]);
         const float4 gb = *reinterpret_cast<const float4*>(&Ds[qloc + 4]);
-        const int e = 8 * half;
-        nd[h][e + 0] = ga.x; nd[h][e + 1] = ga.y; nd[h][e + 2] = ga.z; nd[h][e + 3] = ga.w;
-        nd[h][e + 4] = gb.x; nd[h][e + 5] = gb.y; nd[h][e + 6] = gb.z; nd[h][e + 7] = gb.w;
-      }
-      s[h] = zero16();
-      dp[h] = DROP ? zero16() : nd[h];
-    };
-    auto load_lv = [&](int h) __attribute__((always_inline)) {  // LSE * log2(e), block h
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qloc = 32 * h + 16 * half + 8 * hi;
         const float4 la = *reinterpret_cast<const float4*>(&Ls[qloc]);
         const float4 lb = *reinterpret_cast<const float4*>(&Ls[qloc + 4]);
         const int e = 8 * half;
+        nd[h][e + 0] = ga.x; nd[h][e + 1] = ga.y; nd[h][e + 2] = ga.z; nd[h][e + 3] = ga.w;
+        nd[h][e + 4] = gb.x; nd[h][e + 5] = gb.y; nd[h][e + 6] = gb.z; nd[h][e + 7] = gb.w;
         lv[h][e + 0] = la.x; lv[h][e + 1] = la.y; lv[h][e + 2] = la.z; lv[h][e + 3] = la.w;
         lv[h][e + 4] = lb.x; lv[h][e + 5] = lb.y; lv[h][e + 6] = lb.z; lv[h][e + 7] = lb.w;
       }
-    };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = zero16();
+      // dP starts at -D (the products add dO V^T); with dropout the product must be
+      // masked and scaled first, so it starts at 0.
+      dp[h] = DROP ? zero16() : nd[h];
+    }
+    uint32_t kwd[2][DROP ? 8 : 1];
+    typename T::vec8 pa[2][2], da[2][2];  // [block][half] P and dS as A operands
 
     // Elementwise work on element i of block h: P = exp2(S*sc - LSE*log2e), dS = P (dP - D),
     // with mask and dropout; after elements 7 and 15 the halves are packed.
-    auto elem = [&](int h, int i) __attribute__((always_inline)) {
+    auto elem = [&](int h, int i) {
       if constexpr (DROP) {
         if (i == 0) {
-          // Dropout draws of this lane's key for the block's 32 queries (as in the two-wave
-          // kernel: one Philox call per query pair shared by a lane quad).
+          // Dropout draws of this lane's key for the block's 16 queries (as in the
+          // two-wave kernel: one Philox call per query pair shared by a lane quad).
 #pragma unroll
           for (int sg = 0; sg < 2; ++sg) {
             const int q = q0 + 32 * h + 16 * sg + 8 * hi + 2 * qpos;
@@ -627,7 +619,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
             uint32_t r[4] = {w[0], w[1], w[2], w[3]};
             quad_transpose(r, qpos);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kwd[h][4 * sg + c] = r[c];
+            for (int k = 0; k < 4; ++k) kwd[h][4 * sg + k] = r[k];
           }
         }
       }
@@ -654,55 +646,68 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
       }
     };
 
-    // Operand of op g: a Q or dO row operand (S, dP; block h: + 32h rows, step k: XOR
-    // (k << 5)), or the dO^T / Q^T transpose operand of a dV / dK product (index m: half
-    // m / (2 DB), column block (m / 2) % DB; odd m are dK).
-    typename T::vec8 opnd[NOPS];
-    auto load_op = [&](auto gc) __attribute__((always_inline)) {
-      constexpr int g = decltype(gc)::value;
-      constexpr int kind = Ops::kind(g), h = Ops::blk(g), x = Ops::idx(g);
-      if constexpr (kind < 2) {
-        const int ao = h * 32 * ROWB + (a_off ^ (x << 5));
-        opnd[g] = *reinterpret_cast<const typename T::vec8*>((kind ? dOs : Qs) + ao);
-      } else {
-        const int half = x / (2 * DB), j = (x / 2) % DB;
-        const char* base = ((x & 1) ? Qs : dOs) + h * 32 * ROWB + half * 16 * ROWB;
-        opnd[g] = cat_tr<T>(lds_tr4(base + (t_off0 ^ (j << 6))),
-                            lds_tr4(base + (t_off1 ^ (j << 6))));
-      }
+    // S, dP products: slot u is block u / NS, contraction step u % NS.
+    typename T::vec8 qa[NP], ga[NP];
+    auto load_a = [&](int u) {
+      const int ao = (u / NS) * 32 * ROWB + (a_off ^ ((u % NS) << 5));
+      qa[u] = *reinterpret_cast<const typename T::vec8*>(Qs + ao);
+      ga[u] = *reinterpret_cast<const typename T::vec8*>(dOs + ao);
     };
-    auto do_op = [&](auto gc) __attribute__((always_inline)) {
-      constexpr int g = decltype(gc)::value;
-      constexpr int kind = Ops::kind(g), h = Ops::blk(g), x = Ops::idx(g);
-      if constexpr (kind == 0) {
-        s[h] = mfma32(opnd[g], kf[x], s[h]);
-      } else if constexpr (kind == 1) {
-        dp[h] = mfma32(opnd[g], vf[x], dp[h]);
-      } else {
-        constexpr int half = x / (2 * DB), j = (x / 2) % DB;
-        if constexpr (x & 1) acc_dk[j] = mfma32(da[h][half], opnd[g], acc_dk[j]);
-        else acc_dv[j] = mfma32(pa[h][half], opnd[g], acc_dv[j]);
-      }
+    // dV, dK products: index m = 0 .. 2*NU-1 runs over blocks (h = m / NU), halves, column
+    // blocks j, and the pair (dV with dO^T, dK with Q^T).
+    typename T::vec8 tr[2 * NU];
+    auto load_t = [&](int m) {
+      const int h = m / NU, r = m % NU;
+      const int half = r / (2 * DB), j = (r / 2) % DB;
+      const char* base = ((r & 1) ? Qs : dOs) + h * 32 * ROWB + half * 16 * ROWB;
+      tr[m] = cat_tr<T>(lds_tr4(base + (t_off0 ^ (j << 6))), lds_tr4(base + (t_off1 ^ (j << 6))));
+    };
+    auto update = [&](int m) {
+      const int h = m / NU, r = m % NU;
+      const int half = r / (2 * DB), j = (r / 2) % DB;
+      if (r & 1) acc_dk[j] = mfma32(da[h][half], tr[m], acc_dk[j]);
+      else acc_dv[j] = mfma32(pa[h][half], tr[m], acc_dv[j]);
     };
 
-    load_nd(0);
-    static_for<0, LA>(load_op);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<0, NOPS>([&](auto gc) __attribute__((always_inline)) {
-      constexpr int g = decltype(gc)::value;
-      constexpr int f = Ops::phase(g), t = Ops::pos(g), n = Ops::n_phase(f);
-      if constexpr (t == 0) {  // phase start: D of the next block, LSE of this phase's block
-        if constexpr (f + 1 < NB) load_nd(f + 1);
-        if constexpr (f < NB) load_lv(f);
-      }
-      if constexpr (g + LA < NOPS) load_op(std::integral_constant<int, g + LA>{});
-      do_op(gc);
-      if constexpr (f >= 1 && f <= NB) {  // block f-1's elements [16 t / n, 16 (t + 1) / n)
 #pragma unroll
-        for (int i = (16 * t) / n; i < (16 * (t + 1)) / n; ++i) elem(f - 1, i);
+    for (int u = 0; u < PF; ++u) load_a(u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      if (u + PF < NP) load_a(u + PF);
+      if (u == NP - 1) {
+#pragma unroll
+        for (int m = 0; m < VPF; ++m) load_t(m);
+      }
+      const int h = u / NS, k = u % NS;
+      s[h] = mfma32(qa[u], kf[k], s[h]);
+      // Block 0's elementwise work beside block 1's products: elements
+      // [16 w / NP, 16 (w + 1) / NP) after product w of these 2 NS.
+      const int w = 2 * (u - NS);
+      if (u >= NS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i >= (16 * w) / NP && i < (16 * (w + 1)) / NP) elem(0, i);
+      }
+      dp[h] = mfma32(ga[u], vf[k], dp[h]);
+      if (u >= NS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i >= (16 * (w + 1)) / NP && i < (16 * (w + 2)) / NP) elem(0, i);
       }
       __builtin_amdgcn_sched_barrier(0);
-    });
+    }
+#pragma unroll
+    for (int m = 0; m < 2 * NU; ++m) {
+      if (m + VPF < 2 * NU) load_t(m + VPF);
+      update(m);
+      if (m < NU) {  // block 1's elementwise work beside block 0's products
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i >= (16 * m) / NU && i < (16 * (m + 1)) / NU) elem(1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto run_step = [&](int qt, const char* Qs, const char* dOs, const float* Ls,
                       const float* Ds) {
@@ -1021,8 +1026,8 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
 template <typename T, int D, bool DROP, bool PAD, int DC, int NW = 8>
 hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
   // 128-wide layout (head dims 65 .. 128): one wave per SIMD with K and V in registers,
-  // 1.5% faster than the two-wave kernel at d = 128 and about as fast at d = 96 (which must
-  // run it anyway, so that every head dim of the layout sums in the order of d = 128: its
+  // 1.5% faster than the two-wave kernel at d = 128. d = 96 runs it too, although 0.8%
+  // slower there, so that every head dim of the layout sums in the order of d = 128 (its
   // results equal those of d = 128 on zero-padded tensors bit for bit). On the 64-wide
   // layout a step holds too little matrix work to cover one wave's exponentials, and the
   // two-wave kernel is 3-10% faster.

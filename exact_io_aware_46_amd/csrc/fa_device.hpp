@@ -4,8 +4,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -161,6 +159,7 @@ __device__ __forceinline__ void zero_pad(char* tile, int bytes, int valid, int t
   }
 }
 
+
 // Direct global -> LDS copies (no registers involved) through a buffer resource: lane l's
 // bytes land at lds_base + size * l (lds_base must be the same for the whole wave). They
 // are buffer rather than global loads because the compiler's wait-count pass takes a global
@@ -290,59 +289,6 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&r)[4], int quad_pos) {
     const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
     if (b0) r[k] = recv;
     else r[k + 1] = recv;
-  }
-}
-
-// Matrix-instruction schedule of the one-wave dK/dV step over NB blocks of 32 queries.
-// Phase f (f = 0 .. NB+1) issues the S and dP products of block f (if f < NB: NSP of them,
-// S and dP alternating per contraction step) and the dV, dK products of block f-2 (if
-// f >= 2: NU of them). When both are present they alternate as dV/dK, dV/dK, S, dP
-// (NSP == NU). Op g of the step (0 .. total()-1) is (kind, blk, idx): kind 0 = S, 1 = dP
-// (idx = contraction step), 2 = dV/dK product (idx = its index in the block's NU).
-// Everything folds to constants in a fully unrolled loop over g.
-template <int NB, int NSP, int NU>
-struct PipeOps {
-  static_assert(NSP == NU, "the S/dP and dV/dK products of a block are equally many");
-  static constexpr __device__ __host__ int n_phase(int f) {
-    return (f < NB ? NSP : 0) + (f >= 2 && f < NB + 2 ? NU : 0);
-  }
-  static constexpr __device__ __host__ int total() {
-    int s = 0;
-    for (int f = 0; f < NB + 2; ++f) s += n_phase(f);
-    return s;
-  }
-  static constexpr __device__ __host__ int phase(int g) {
-    int f = 0;
-    while (g >= n_phase(f)) g -= n_phase(f++);
-    return f;
-  }
-  static constexpr __device__ __host__ int pos(int g) {  // index within the phase
-    int f = 0;
-    while (g >= n_phase(f)) g -= n_phase(f++);
-    return g;
-  }
-  static constexpr __device__ __host__ int kind(int g) {
-    const int f = phase(g), t = pos(g);
-    if (f >= 2 && f < NB) return t % 4 < 2 ? 2 : t % 4 - 2;
-    return f < NB ? t % 2 : 2;
-  }
-  static constexpr __device__ __host__ int blk(int g) {
-    return kind(g) == 2 ? phase(g) - 2 : phase(g);
-  }
-  static constexpr __device__ __host__ int idx(int g) {
-    const int f = phase(g), t = pos(g);
-    if (f >= 2 && f < NB) return t % 4 < 2 ? 2 * (t / 4) + t % 4 : t / 4;
-    return f < NB ? t / 2 : t;
-  }
-};
-
-// Compile-time loop: calls f(std::integral_constant<int, I>{}) for I = B .. E-1, so that
-// values derived from I are constant expressions (array indices, schedule lookups).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
   }
 }
 
