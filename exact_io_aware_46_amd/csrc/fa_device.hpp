@@ -159,7 +159,6 @@ __device__ __forceinline__ void zero_pad(char* tile, int bytes, int valid, int t
   }
 }
 
-
 // Direct global -> LDS copies (no registers involved) through a buffer resource: lane l's
 // bytes land at lds_base + size * l (lds_base must be the same for the whole wave). They
 // are buffer rather than global loads because the compiler's wait-count pass takes a global
