@@ -67,7 +67,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // Read as uniform: per-wave tests become scalar branches and wave-derived values live in
+  // SGPRs (22 fewer VGPRs at d = 128, 2.5% faster). The backward kernels measured slower
+  // with the same change and keep the plain index.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
