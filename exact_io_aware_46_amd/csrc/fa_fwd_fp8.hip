@@ -114,7 +114,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // Read as uniform (scalar per-wave tests, wave-derived values in SGPRs): 2.3% faster.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
