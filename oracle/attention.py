@@ -61,13 +61,16 @@ notes of the repository):
     with one float32 descale per tensor: q = descale_q * decode(Q8), likewise k and v.
   - S = scale * q k^T in exact arithmetic, masked as above.
   - In log2 units t = S * log2(e). With m = ceil(max_j t_j) over the row's allowed keys,
-    P_j = 2^(t_j - m) lies in (0, 1].
+    the scaled probabilities P_j = 2^(t_j - m + 6) lie in (0, 64]: the row's largest is in
+    (32, 64], so every probability down to 2^-12 of it lies in E4M3's normal range
+    (smallest normal 2^-6), and the headroom up to 448 (2^8.8) is left for a one-pass
+    kernel whose running reference trails the row maximum.
   - P_j is rounded to E4M3, nearest with ties to even, subnormals included, giving Pq_j.
     l = sum_j P_j is left unrounded.
   - O = descale_v * sum_j Pq_j decode(V8_j) / l, and LSE = ln sum_j exp(S_j).
-  - The reference m is an integer power of two, so a kernel whose running reference is any
-    integer (in log2 units) quantises the same P, scaled by a power of two. That scaling
-    commutes with the rounding wherever both sides are in the normal range.
+  - The reference m is an integer, so a kernel whose running reference is any integer (in
+    log2 units) quantises the same P, scaled by a power of two. That scaling commutes with
+    the rounding wherever both sides are in the normal range.
 * a row with no allowed key has O = 0, LSE = -inf and contributes nothing to gradients;
 * backward is the derivative of the scalar L = sum(dO * O) with respect to Q, K, V:
   dV = P^T dO, dP = dO V^T, D_i = sum_c dO_ic O_ic, dS = P * (dP - D),
@@ -362,6 +365,7 @@ def _e4m3_table() -> np.ndarray:
 
 E4M3 = _e4m3_table()
 E4M3_MAX = 448.0
+FP8_P_SHIFT = 6   # log2 of the factor the probabilities are scaled by before rounding
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -407,7 +411,7 @@ def head_forward_fp8(Q8, K8, V8, descale, scale, causal=False, blockmask=None,
         t = S * (1.0 / np.log(2.0))
         with np.errstate(invalid="ignore"):
             m = np.ceil(np.where(live, np.max(np.where(np.isfinite(t), t, -np.inf), axis=1), 0))
-        P = np.where(np.isfinite(t), np.exp2(t - m[:, None]), 0.0)
+        P = np.where(np.isfinite(t), np.exp2(t - m[:, None] + FP8_P_SHIFT), 0.0)
         l = P.sum(axis=1)
         Pq = e4m3_round(P)
         num = Pq @ Vh

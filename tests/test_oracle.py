@@ -651,8 +651,9 @@ def test_dropout_delta_two_ways():
 
 
 # ------------------------------------------------------------------ FP8 forward
-# Reading: Q, K, V as OCP E4M3 codes with per-tensor descales; P = 2^(t - ceil(max t)) is
-# rounded to E4M3 (nearest, ties to even) before P V; l and LSE use the unrounded P.
+# Reading: Q, K, V as OCP E4M3 codes with per-tensor descales; the scaled probability
+# P = 2^(t - ceil(max t) + 6) is rounded to E4M3 (nearest, ties to even) before P V; l and
+# LSE use the unrounded P.
 
 def test_e4m3_decode_matches_torch_and_known_codes():
     codes = np.arange(256, dtype=np.uint8)
@@ -702,18 +703,19 @@ def test_fp8_forward_matches_brute_force():
               for j in range(i + 1)]
         t = [x / math.log(2.0) for x in sc]
         m = math.ceil(max(t))
-        P = [2.0 ** (x - m) for x in t]
+        P = [2.0 ** (x - m + 6) for x in t]
         Pq = [float(torch.tensor([p], dtype=torch.float32).to(torch.float8_e4m3fn).double())
               for p in P]
         l = math.fsum(P)
-        assert abs(L[i] - (m * math.log(2.0) + math.log(l))) < 1e-12
+        assert abs(L[i] - ((m - 6) * math.log(2.0) + math.log(l))) < 1e-12
         for c in range(d):
             want = 0.5 * math.fsum(Pq[j] * dec(v8[j, c]) for j in range(i + 1)) / l
             assert abs(O[i, c] - want) < 1e-12, (i, c)
 
 
 def test_fp8_forward_equal_scores_closed_form():
-    # Identical keys: every P_j = p0 = 2^(t0 - ceil t0), so O = descale_v * (Pq0 / p0) * mean(V).
+    # Identical keys: every P_j = p0 = 2^(t0 - ceil t0 + 6), so
+    # O = descale_v * (Pq0 / p0) * mean(V).
     N, d = 40, 16
     q8 = _fp8_codes((N, d), 137)
     k8 = np.repeat(_fp8_codes((1, d), 138), N, axis=0)
@@ -722,7 +724,7 @@ def test_fp8_forward_equal_scores_closed_form():
     O, L = orc.head_forward_fp8(q8, k8, v8, desc, 0.3)
     Q, K = orc.e4m3_decode(q8), 0.5 * orc.e4m3_decode(k8)
     t0 = float(np.float32(0.3)) * (Q @ K[0]) / math.log(2.0)
-    p0 = 2.0 ** (t0 - np.ceil(t0))
+    p0 = 2.0 ** (t0 - np.ceil(t0) + 6)
     ratio = orc.e4m3_round(p0) / p0
     want = 2.0 * ratio[:, None] * orc.e4m3_decode(v8).mean(axis=0)[None, :]
     np.testing.assert_allclose(O, want, rtol=1e-12, atol=1e-13)
@@ -731,7 +733,7 @@ def test_fp8_forward_equal_scores_closed_form():
 
 def test_fp8_forward_is_plain_attention_within_the_rounding_of_p():
     # |O_fp8 - O| <= descale_v * (2^-4 sum_j P_j |V_j| + 2^-10 sum_j |V_j|) / l, from
-    # |Pq - P| <= max(2^-4 P, 2^-10); LSE is unchanged.
+    # |Pq - P| <= max(2^-4 P, 2^-10) for the scaled P = 2^(t - m + 6); LSE is unchanged.
     N, d = 200, 32
     q8, k8, v8 = (_fp8_codes((1, 2, N, d), s) for s in (141, 142, 143))
     desc = (0.9, 1.1, 0.7)
@@ -744,7 +746,7 @@ def test_fp8_forward_is_plain_attention_within_the_rounding_of_p():
     t = np.float32(0.2) * np.einsum("bhid,bhjd->bhij", q, k) / math.log(2.0)
     t = np.where(np.tril(np.ones((N, N), bool)), t, -np.inf)
     m = np.ceil(t.max(-1))
-    l = np.exp2(t - m[..., None]).sum(-1)
+    l = np.exp2(t - m[..., None] + 6).sum(-1)
     csum = np.cumsum(np.abs(v), axis=2)                          # causal sum_j |V_j|
     bound = desc[2] * (2.0 ** -4 * Oa + 2.0 ** -10 * csum / l[..., None])
     assert (np.abs(O - O0) <= bound + 1e-12).all()
@@ -767,3 +769,45 @@ def test_planted_fp8_mistakes_are_caught():
         orc.e4m3_round = orig_round
     bad, _ = orc.head_forward_fp8(q8, k8, v8, (0.75, 1.25, 1.0), 0.6, causal=True)
     assert np.abs(bad - ref).max() > 1e-6
+
+
+def test_planted_fp8_unscaled_probabilities_are_caught():
+    # Rounding 2^(t - m) instead of 2^(t - m + 6) changes every probability below 2^-6 of the
+    # row maximum (subnormal for the unscaled one, normal for the scaled one): on wide scores
+    # the two definitions differ, so the brute-force pin above fixes the shift.
+    N, d = 40, 16
+    q8, k8, v8 = (_fp8_codes((1, 1, N, d), s, sd=2.0) for s in (145, 146, 147))
+    desc = (1.0, 1.0, 0.5)
+    ref, _ = orc.forward_fp8(q8, k8, v8, desc, 0.35)
+    old = orc.FP8_P_SHIFT
+    try:
+        orc.FP8_P_SHIFT = 0
+        bad, _ = orc.forward_fp8(q8, k8, v8, desc, 0.35)
+    finally:
+        orc.FP8_P_SHIFT = old
+    assert np.abs(bad - ref).max() > 1e-6
+
+
+@pytest.mark.parametrize("causal,window,kv,bm", [
+    (True, None, None, None),
+    (False, (50, 10), [300, 170], None),
+    (True, None, [300, 99], [[1, 0, 1], [1, 1, 0], [0, 1, 1]]),
+])
+def test_fp8_rows_equal_the_whole_forward(causal, window, kv, bm):
+    # forward_fp8_rows (sampled rows, used at sizes where the whole forward is too slow)
+    # returns the rows of forward_fp8, up to the fp64 summation order of a one-row product
+    # against a whole-panel one (a few ulp).
+    N, d = 300, 32
+    B = 1 if kv is None else len(kv)
+    q8, k8, v8 = (_fp8_codes((B, 2, N, d), s) for s in (148, 149, 150))
+    desc = (0.8, 1.2, 0.6)
+    kvn = None if kv is None else np.array(kv, dtype=np.int32)
+    bmn = None if bm is None else np.array(bm, dtype=np.uint8)
+    O, L = orc.forward_fp8(q8, k8, v8, desc, 0.3, causal, bmn, kvn, window)
+    rng = np.random.Generator(np.random.PCG64(151))
+    sel = [(int(rng.integers(B)), int(rng.integers(2)), int(rng.integers(N))) for _ in range(12)]
+    sel += [(B - 1, 1, N - 1), (0, 0, 0)]
+    Or, Lr = orc.forward_fp8_rows(q8, k8, v8, desc, 0.3, sel, causal, bmn, kvn, window)
+    idx = tuple(np.array(sel).T)
+    np.testing.assert_allclose(Lr, L[idx], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Or, O[idx], rtol=1e-12, atol=1e-14)
