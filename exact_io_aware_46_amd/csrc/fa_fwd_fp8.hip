@@ -3,9 +3,10 @@
 // brought FP8 to the forward pass ("IO感知计算如何重塑Transformer内存优化技术格局",
 // bxzpzcl.cn, section 技术演进时间线); the pages give no quantisation policy, and the
 // one used here is: scores from the E4M3 products in fp32; softmax statistics in fp32; the
-// probabilities rounded to E4M3 (nearest even) for the P V product, against a running
-// reference that is an integer in log2 units; the normaliser from the unrounded
-// probabilities. The tiling, online softmax and fusion are those of the bf16 forward.
+// probabilities, scaled by 2^6 against a running reference that is an integer in log2
+// units, rounded to E4M3 (nearest even) for the P V product; the normaliser from the
+// unrounded probabilities. The tiling, online softmax and fusion are those of the bf16
+// forward.
 //
 // gfx950 mapping:
 //   v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales: 32x32 outputs, 64-deep
@@ -20,9 +21,12 @@
 //     32 + 16h + (b - 16): the P bytes are the two score blocks' accumulators in order,
 //     and the V^T bytes are two 16-byte chunks of a row of a transposed V tile. V^T is
 //     written by a small transpose pass into the caller's workspace.
-//   Reference max: raised only when a tile's max exceeds it by more than 8 (log2 units),
-//   and always to an integer (the ceiling), so P <= 2^8 fits E4M3 and every P is the
-//   reference-max-rounded-up P times a power of two: E4M3 rounding commutes with that.
+//   Reference max: always an integer (the ceiling of a tile max), raised only when a tile's
+//   max exceeds it by more than 2.8 (log2 units). The probabilities are formed as
+//   P = 2^(t - m + 6): the row's largest lies in (32, 445.7] (2^8.8 < 448, the largest
+//   finite E4M3 value), and probabilities down to 2^-12 of the row maximum stay in E4M3's
+//   normal range. Every P is the P of the reference ceil(row max) times a power of two,
+//   and E4M3 rounding commutes with that in the normal range.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -62,20 +66,23 @@ __device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
 
-// V [N][D] -> V^T [D][Np] for one (b, h) and 64 keys (columns past N are zero). Loads the
-// 64 x D block row-major into LDS (rows padded by 4 bytes so the column reads below fall
-// in different banks), then each thread turns a 4-key x 4-byte block into 4 words along
-// the keys.
+// V [N][D] -> V^T [D][Np] for one (b, h) and 64 keys. Columns of keys past N or past the
+// batch entry's valid length are zero, so the caller's bytes there (NaN codes included)
+// never reach P V, where a masked probability is the E4M3 code 0. Loads the 64 x D block
+// row-major into LDS (rows padded by 4 bytes so the column reads below fall in different
+// banks), then each thread turns a 4-key x 4-byte block into 4 words along the keys.
 template <int D>
 __global__ __launch_bounds__(256) void vt_fp8_kernel(const uint8_t* __restrict__ v,
-                                                     uint8_t* __restrict__ vt, int N, int Np) {
+                                                     uint8_t* __restrict__ vt, int N, int Np,
+                                                     int H, const int32_t* __restrict__ kv_len) {
   constexpr int LW = D / 4 + 1;  // words per padded LDS row
   __shared__ uint32_t tile[64 * LW];
   const int bh = (int)blockIdx.y, k0 = (int)blockIdx.x * 64, tid = (int)threadIdx.x;
+  const int klim = kv_len ? min(N, max(kv_len[bh / H], 0)) : N;
   const uint8_t* src = v + (size_t)bh * N * D;
   for (int e = tid; e < 64 * (D / 4); e += 256) {
     const int r = e / (D / 4), c = e % (D / 4);
-    tile[r * LW + c] = k0 + r < N ? ldg4(src + (size_t)(k0 + r) * D + 4 * c) : 0u;
+    tile[r * LW + c] = k0 + r < klim ? ldg4(src + (size_t)(k0 + r) * D + 4 * c) : 0u;
   }
   __syncthreads();
   uint8_t* dst = vt + (size_t)bh * D * Np;
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
     return kt;
   };
   // Key tile kt -> stage: K rows (rows at or past klim fetch row klim-1, masked later) and
-  // the V^T columns k0 .. k0+63 (zero past N in the workspace).
+  // the V^T columns k0 .. k0+63 (zero past klim in the workspace).
   // Both copies go through buffer resources based at the tile (see buf_rsrc). The V^T
   // tile spans D rows of the transposed workspace: its offsets, below D * Np <= N * d +
   // 63 d, stay under 2^32 because the C ABI keeps N * d below 2^31 (offsets and sizes are
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   f32x16 acc[DB];
 #pragma unroll
   for (int j = 0; j < DB; ++j) acc[j] = zero16();
-  float m_run = -kInf;  // integer reference max, log2 units
+  float m_run = -kInf;  // integer reference max, log2 units (P = 2^(t - m_run + 6))
   float l_run = 0.f;
 
   // LDS operand offsets. K: lane row r reads key pi(r), chunks 4*st + 2*hi + e (e = 0, 1);
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = xhalf_max(mx) * p.sc;
-    const bool up = mx > m_run + 8.f;
+    const bool up = mx > m_run + 2.8f;
     if (__builtin_amdgcn_ballot_w64(up)) {
       const float m_new = up ? ceilf(mx) : m_run;
       const float alpha = up ? fast_exp2(m_run - m_new) : 1.f;  // an exact power of two
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][i] *= alpha;
     }
-    const float m_use = m_run == -kInf ? 0.f : m_run;
+    const float m_use = m_run == -kInf ? 0.f : m_run - 6.f;
 
     float lsum = 0.f;
 #pragma unroll
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
         *reinterpret_cast<u32x2*>(orow + j * 32 + 8 * g + 4 * hi) = w;
       }
     if (hi == 0)
-      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -kInf;
+      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? (m_run - 6.f) * kLn2 + logf(l_tot) : -kInf;
   }
 }
 
@@ -334,9 +341,11 @@ hipError_t launch_fwd_fp8(const Fp8Params& p, const uint8_t* v, uint8_t* vt, int
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 tgrid((unsigned)(p.Np / 64), bh);
   if (d == 128)
-    hipLaunchKernelGGL((vt_fp8_kernel<128>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np);
+    hipLaunchKernelGGL((vt_fp8_kernel<128>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
+                       p.H, p.kv_len);
   else
-    hipLaunchKernelGGL((vt_fp8_kernel<64>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np);
+    hipLaunchKernelGGL((vt_fp8_kernel<64>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
+                       p.H, p.kv_len);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((p.N + 255) / 256) * bh);

@@ -181,11 +181,13 @@ int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const
  *     subnormals; S.1111.111 is NaN; largest finite 448), [B][H][N][d] row-major, one
  *     byte per element; the values are descale_q * q, descale_k * k, descale_v * v.
  *   S = scale * (descale_q q)(descale_k k)^T, masked as in fa_fwd_window. In log2 units the
- *     probabilities are P = 2^(S log2(e) - m) for an integer reference m of the row. Each
- *     P is rounded to E4M3 (nearest, ties to even) for the product with V, and the
- *     normaliser is the sum of the unrounded P. m is the row's running maximum rounded up,
- *     so the rounded P equal, up to a power of two, those of the reference
- *     m = ceil(row max) wherever both lie in the E4M3 normal range.
+ *     scaled probabilities are P = 2^(S log2(e) - m + 6) for an integer reference m of the
+ *     row. Each P is rounded to E4M3 (nearest, ties to even) for the product with V, and
+ *     the normaliser is the sum of the unrounded P. m is a running maximum rounded up (an
+ *     integer at most 3 below ceil(row max), so P <= 2^8.8 < 448), and the rounded P equal,
+ *     up to a power of two, those of the reference m = ceil(row max) wherever both lie in
+ *     the E4M3 normal range, which holds for every P down to 2^-12 of the row's largest.
+ *     Keys masked by kv_len contribute nothing, whatever bytes k and v hold there.
  *   o: DEVICE bf16 [B][H][N][d] = descale_v * (rounded P) v / normaliser; lse: DEVICE fp32
  *     [B][H][N], the natural-log logsumexp of the scores (-inf for a row with no allowed
  *     key, whose o is 0).
