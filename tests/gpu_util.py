@@ -143,39 +143,23 @@ def run_fp8(q8, k8, v8, scale, descale, causal=False, blockmask=None, kv_len=Non
     return to_f64(o), to_f64(lse), ws
 
 
-def fp8_rounding_bound(q8, k8, v8, descale, scale, O_ref, rows_of, allowed_of):
-    """Elementwise bound on |O_kernel - O_oracle| for the FP8 forward. Both round
-    P = 2^(t - m) to E4M3 against integer references that differ by a power of two 2^k
-    (k >= 0, the kernel's reference is the lower one):
-      - in the normal range the two roundings agree after scaling, except where fp32
-        scores put P on the other side of a rounding tie: at most one E4M3 step,
-        2^-3 P;
-      - where the oracle's P is below 2^-6 (subnormal for it) the two differ by at most
-        2^-9 on the oracle's scale (half a subnormal step each).
-    So |dO| <= descale_v (2^-3 sum_j P_j |V_j| + 2^-9 sum_{P_j < 2^-6} |V_j|) / l, plus the
-    bf16 rounding of O (2^-8 |O| with slack) and 1e-4 for fp32 accumulation.
-    rows_of(b, h) -> query indices of the rows in O_ref[b, h]; allowed_of(b, h, rows) ->
-    boolean [rows][N]."""
-    from oracle import attention as orc
-    dq, dk, dv = (float(np.float32(x)) for x in descale)
-    s = float(np.float32(scale))
-    bound = np.zeros_like(O_ref)
-    B, H = q8.shape[:2]
-    for b in range(B):
-        for h in range(H):
-            rows = rows_of(b, h)
-            if len(rows) == 0:
-                continue
-            Q = dq * orc.e4m3_decode(q8[b, h][rows])
-            K = dk * orc.e4m3_decode(k8[b, h])
-            Va = np.abs(orc.e4m3_decode(v8[b, h]))
-            ok = allowed_of(b, h, rows)
-            t = np.where(ok, s * (Q @ K.T) / np.log(2.0), -np.inf)
-            live = ok.any(axis=1)
-            m = np.ceil(np.where(live, t.max(axis=1), 0.0))
-            P = np.where(ok, np.exp2(t - m[:, None]), 0.0)
-            l = np.where(live, P.sum(axis=1), 1.0)
-            big = (2.0 ** -3) * (P @ Va) / l[:, None]
-            sub = (2.0 ** -9) * (np.where(ok & (P < 2.0 ** -6), 1.0, 0.0) @ Va) / l[:, None]
-            bound[b, h] = dv * (big + sub)
-    return bound + 2.0 ** -8 * np.abs(O_ref) + 1e-4
+def count_raises(t, ok, tile, thresh, integer):
+    """How many times each row's running reference is raised after its first value, under
+    the forward kernels' rule: key tiles of ``tile`` keys in order; a tile whose largest
+    allowed score exceeds the reference by more than ``thresh`` (log2 units) raises it to
+    that score (rounded up if ``integer``). ``t`` [r, N] scores in log2 units, ``ok``
+    [r, N] allowed pairs. Used to show that a test's inputs reach the rescaling code."""
+    r, N = t.shape
+    nt = -(-N // tile)
+    tt = np.full((r, nt * tile), -np.inf)
+    tt[:, :N] = np.where(ok, t, -np.inf)
+    tmax = tt.reshape(r, nt, tile).max(axis=2)
+    m = np.full(r, -np.inf)
+    cnt = np.zeros(r, dtype=np.int64)
+    for j in range(nt):
+        mx = tmax[:, j]
+        with np.errstate(invalid="ignore"):
+            up = mx > m + thresh
+        cnt += up & np.isfinite(m)
+        m = np.where(up, np.ceil(mx) if integer else mx, m)
+    return cnt
