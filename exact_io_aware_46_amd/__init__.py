@@ -82,18 +82,75 @@ def strerror(status: int) -> str:
 
 
 # ------------------------------------------------------------- marshalling
+#
+# Each tensor argument is checked against what the C ABI will read or write through its
+# pointer, before the call: of the element type the entry point takes, with exactly the
+# number of elements the shape (B, H, N, d) implies (the workspace: at least the bytes
+# the library asks for), then on the GPU and contiguous. A raw integer is passed through
+# as a device address without checks. Violations raise ValueError and nothing is called.
 
-def _dev_ptr(t, name):
-    """Device pointer of a torch tensor (None -> NULL). Raises for host tensors."""
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr()
+def _dtypes(kind):
+    import torch
+    return {"bf16": (torch.bfloat16,), "f16": (torch.float16,), "f32": (torch.float32,),
+            "i32": (torch.int32,), "mask": (torch.uint8, torch.bool),
+            "fp8": (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))}[kind]
+
+
+class _Args:
+    """One call's pointer arguments: ``add`` checks type and size and returns the device
+    pointer (None -> NULL); ``ready`` then checks that every tensor is on the GPU and
+    contiguous."""
+
+    def __init__(self, B, H, N, d):
+        self.B, self.H, self.N, self.d = int(B), int(H), int(N), int(d)
+        self.t = self.B * self.H * self.N * self.d     # elements of q, k, v, o, ...
+        self.rows = self.B * self.H * self.N           # elements of lse, delta
+        self.mask = ((self.N + 127) // 128) ** 2       # elements of the block table
+        self._seen = []
+
+    def add(self, t, name, kind=None, numel=None, min_bytes=None):
+        if t is None:
+            return None
+        if isinstance(t, int):
+            return t
+        if kind is not None and t.dtype not in _dtypes(kind):
+            raise ValueError(f"{name} must have dtype "
+                             f"{' or '.join(map(str, _dtypes(kind)))}, got {t.dtype}")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+        if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+            raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, "
+                             f"needs {min_bytes}")
+        self._seen.append((name, t))
+        return t.data_ptr()
+
+    def ready(self):
+        for name, t in self._seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a GPU tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+
+    def fwd(self, kind, q, k, v, o, lse):
+        return [self.add(q, "q", kind, self.t), self.add(k, "k", kind, self.t),
+                self.add(v, "v", kind, self.t), self.add(o, "o", kind, self.t),
+                self.add(lse, "lse", "f32", self.rows)]
+
+    def bwd(self, kind, q, k, v, o, lse, dO, dq, dk, dv):
+        return [self.add(q, "q", kind, self.t), self.add(k, "k", kind, self.t),
+                self.add(v, "v", kind, self.t), self.add(o, "o", kind, self.t),
+                self.add(lse, "lse", "f32", self.rows), self.add(dO, "dO", kind, self.t),
+                self.add(dq, "dq", kind, self.t), self.add(dk, "dk", kind, self.t),
+                self.add(dv, "dv", kind, self.t)]
+
+    def blockmask(self, t):
+        return self.add(t, "blockmask", "mask", self.mask)
+
+    def kv_len(self, t):
+        return self.add(t, "kv_len", "i32", self.B)
+
+    def workspace(self, t, nbytes):
+        return self.add(t, "workspace", None, None, nbytes)
 
 
 def _stream_ptr(stream):
@@ -110,34 +167,44 @@ def _check(status, where):
         raise FAError(status, where)
 
 
+def _kind(dtype):
+    if dtype == DTYPE_BF16:
+        return "bf16"
+    if dtype == DTYPE_F16:
+        return "f16"
+    return None  # the library rejects it (FA_ERR_DTYPE)
+
+
+def _call(a, name, *args):
+    a.ready()
+    _check(getattr(lib(), name)(*args), name)
+
+
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, stream=None):
-    _check(lib().fa_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                        _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
-                        int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                        _stream_ptr(stream)), "fa_fwd")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd", *a.fwd("bf16", q, k, v, o, lse), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), _stream_ptr(stream))
 
 
 def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
               stream=None):
-    _check(lib().fa_fwd_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                           _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
-                           int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                           _dev_ptr(kv_len, "kv_len"), _stream_ptr(stream)), "fa_fwd_ex")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd_ex", *a.fwd("bf16", q, k, v, o, lse), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), _stream_ptr(stream))
 
 
 def fa_fwd_window(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
                   window_left=-1, window_right=-1, stream=None):
-    _check(lib().fa_fwd_window(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                               _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
-                               int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                               _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
-                               _stream_ptr(stream)), "fa_fwd_window")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd_window", *a.fwd("bf16", q, k, v, o, lse), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), int(window_left),
+          int(window_right), _stream_ptr(stream))
 
 
 def fa_bwd_preprocess(o, dO, delta, B, H, N, d, stream=None):
-    _check(lib().fa_bwd_preprocess(_dev_ptr(o, "o"), _dev_ptr(dO, "dO"),
-                                   _dev_ptr(delta, "delta"), B, H, N, d,
-                                   _stream_ptr(stream)), "fa_bwd_preprocess")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_preprocess", a.add(o, "o", "bf16", a.t), a.add(dO, "dO", "bf16", a.t),
+          a.add(delta, "delta", "f32", a.rows), B, H, N, d, _stream_ptr(stream))
 
 
 def fa_bwd_workspace_bytes(B, H, N, d) -> int:
@@ -146,85 +213,72 @@ def fa_bwd_workspace_bytes(B, H, N, d) -> int:
 
 def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
            workspace=None, stream=None):
-    _check(lib().fa_bwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                        _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
-                        _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N, d,
-                        float(scale), int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                        _dev_ptr(workspace, "workspace"), _stream_ptr(stream)), "fa_bwd")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd", *a.bwd("bf16", q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d,
+          float(scale), int(bool(causal)), a.blockmask(blockmask),
+          a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 def fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
               kv_len=None, workspace=None, stream=None):
-    _check(lib().fa_bwd_ex(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                           _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
-                           _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N,
-                           d, float(scale), int(bool(causal)),
-                           _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
-                           _dev_ptr(workspace, "workspace"), _stream_ptr(stream)), "fa_bwd_ex")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_ex", *a.bwd("bf16", q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d,
+          float(scale), int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len),
+          a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 def fa_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
                   blockmask=None, kv_len=None, window_left=-1, window_right=-1,
                   workspace=None, stream=None):
-    _check(lib().fa_bwd_window(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                               _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
-                               _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H,
-                               N, d, float(scale), int(bool(causal)),
-                               _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
-                               int(window_left), int(window_right),
-                               _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
-           "fa_bwd_window")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_window", *a.bwd("bf16", q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d,
+          float(scale), int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len),
+          int(window_left), int(window_right),
+          a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None, kv_len=None,
                window_left=-1, window_right=-1, stream=None):
-    _check(lib().fa_fwd_f16(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
-                            int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                            _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
-                            _stream_ptr(stream)), "fa_fwd_f16")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd_f16", *a.fwd("f16", q, k, v, o, lse), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), int(window_left),
+          int(window_right), _stream_ptr(stream))
 
 
 def fa_bwd_preprocess_f16(o, dO, delta, B, H, N, d, stream=None):
-    _check(lib().fa_bwd_preprocess_f16(_dev_ptr(o, "o"), _dev_ptr(dO, "dO"),
-                                       _dev_ptr(delta, "delta"), B, H, N, d,
-                                       _stream_ptr(stream)), "fa_bwd_preprocess_f16")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_preprocess_f16", a.add(o, "o", "f16", a.t), a.add(dO, "dO", "f16", a.t),
+          a.add(delta, "delta", "f32", a.rows), B, H, N, d, _stream_ptr(stream))
 
 
 def fa_bwd_f16(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0, blockmask=None,
                kv_len=None, window_left=-1, window_right=-1, workspace=None, stream=None):
-    _check(lib().fa_bwd_f16(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), _dev_ptr(dO, "dO"),
-                            _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, N,
-                            d, float(scale), int(bool(causal)),
-                            _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
-                            int(window_left), int(window_right),
-                            _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
-           "fa_bwd_f16")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_f16", *a.bwd("f16", q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d,
+          float(scale), int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len),
+          int(window_left), int(window_right),
+          a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 def fa_fwd_dropout(dtype, q, k, v, o, lse, B, H, N, d, scale, causal=0, blockmask=None,
                    kv_len=None, window_left=-1, window_right=-1, dropout_p=0.0, seed=0,
                    offset=0, stream=None):
-    _check(lib().fa_fwd_dropout(int(dtype), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
-                                _dev_ptr(v, "v"), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H,
-                                N, d, float(scale), int(bool(causal)),
-                                _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
-                                int(window_left), int(window_right), float(dropout_p),
-                                int(seed), int(offset), _stream_ptr(stream)), "fa_fwd_dropout")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd_dropout", int(dtype), *a.fwd(_kind(dtype), q, k, v, o, lse), B, H, N, d,
+          float(scale), int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len),
+          int(window_left), int(window_right), float(dropout_p), int(seed), int(offset),
+          _stream_ptr(stream))
 
 
 def fa_bwd_dropout(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
                    blockmask=None, kv_len=None, window_left=-1, window_right=-1,
                    dropout_p=0.0, seed=0, offset=0, workspace=None, stream=None):
-    _check(lib().fa_bwd_dropout(int(dtype), _dev_ptr(q, "q"), _dev_ptr(k, "k"),
-                                _dev_ptr(v, "v"), _dev_ptr(o, "o"), _dev_ptr(lse, "lse"),
-                                _dev_ptr(dO, "dO"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
-                                _dev_ptr(dv, "dv"), B, H, N, d, float(scale), int(bool(causal)),
-                                _dev_ptr(blockmask, "blockmask"), _dev_ptr(kv_len, "kv_len"),
-                                int(window_left), int(window_right), float(dropout_p),
-                                int(seed), int(offset), _dev_ptr(workspace, "workspace"),
-                                _stream_ptr(stream)), "fa_bwd_dropout")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_dropout", int(dtype),
+          *a.bwd(_kind(dtype), q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), int(window_left),
+          int(window_right), float(dropout_p), int(seed), int(offset),
+          a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 def fa_fwd_fp8_workspace_bytes(B, H, N, d):
@@ -234,13 +288,13 @@ def fa_fwd_fp8_workspace_bytes(B, H, N, d):
 def fa_fwd_fp8(q8, k8, v8, o, lse, B, H, N, d, scale, descale_q, descale_k, descale_v,
                causal=0, blockmask=None, kv_len=None, window_left=-1, window_right=-1,
                workspace=None, stream=None):
-    _check(lib().fa_fwd_fp8(_dev_ptr(q8, "q"), _dev_ptr(k8, "k"), _dev_ptr(v8, "v"),
-                            _dev_ptr(o, "o"), _dev_ptr(lse, "lse"), B, H, N, d, float(scale),
-                            float(descale_q), float(descale_k), float(descale_v),
-                            int(bool(causal)), _dev_ptr(blockmask, "blockmask"),
-                            _dev_ptr(kv_len, "kv_len"), int(window_left), int(window_right),
-                            _dev_ptr(workspace, "workspace"), _stream_ptr(stream)),
-           "fa_fwd_fp8")
+    a = _Args(B, H, N, d)
+    _call(a, "fa_fwd_fp8", a.add(q8, "q", "fp8", a.t), a.add(k8, "k", "fp8", a.t),
+          a.add(v8, "v", "fp8", a.t), a.add(o, "o", "bf16", a.t),
+          a.add(lse, "lse", "f32", a.rows), B, H, N, d, float(scale), float(descale_q),
+          float(descale_k), float(descale_v), int(bool(causal)), a.blockmask(blockmask),
+          a.kv_len(kv_len), int(window_left), int(window_right),
+          a.workspace(workspace, fa_fwd_fp8_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
 
 
 # ------------------------------------------------- allocating convenience layer

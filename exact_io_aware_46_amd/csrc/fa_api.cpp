@@ -196,36 +196,55 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 }  // extern "C"
 
-namespace {
+namespace fa {
 
-int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-             const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
-             uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
-             const uint8_t* blockmask, const int32_t* kv_len, int window_left, int window_right,
-             float dropout_p, uint64_t seed, uint32_t offset, void* workspace, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+int bwd_check(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+              const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+              int B, int H, int N, int d, float scale, const int32_t* kv_len,
+              float dropout_p) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dO, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, kWsAlign) || (kv_len && !aligned(kv_len, 4)))
+      !aligned(lse, 4) || (kv_len && !aligned(kv_len, 4)))
     return FA_ERR_ALIGN;
   const size_t rows = (size_t)B * H * N;
   const size_t tbytes = rows * d * 2;
-  const Range outs[4] = {span(dq, tbytes), span(dk, tbytes), span(dv, tbytes),
-                         span(workspace, fa_bwd_workspace_bytes(B, H, N, d))};
+  const Range outs[3] = {span(dq, tbytes), span(dk, tbytes), span(dv, tbytes)};
   const Range ins[6] = {span(q, tbytes), span(k, tbytes), span(v, tbytes),
                         span(o, tbytes), span(dO, tbytes), span(lse, rows * 4)};
-  for (int a = 0; a < 4; ++a) {
-    for (int b = a + 1; b < 4; ++b)
+  for (int a = 0; a < 3; ++a) {
+    for (int b = a + 1; b < 3; ++b)
       if (overlap(outs[a], outs[b])) return FA_ERR_ALIAS;
     for (int b = 0; b < 6; ++b)
       if (overlap(outs[a], ins[b])) return FA_ERR_ALIAS;
   }
+  if (!(dropout_p >= 0.f && dropout_p < 1.f)) return FA_ERR_DROPOUT;
+  return FA_OK;
+}
+
+int bwd_entry(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+              const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
+              uint16_t* dk, uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
+              const uint8_t* blockmask, const int32_t* kv_len, int window_left,
+              int window_right, float dropout_p, uint64_t seed, uint32_t offset,
+              void* workspace, void* stream) {
+  int st = bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, kv_len, dropout_p);
+  if (st != FA_OK) return st;
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, kWsAlign)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * N;
+  const size_t tbytes = rows * d * 2;
+  const Range rw = span(workspace, fa_bwd_workspace_bytes(B, H, N, d));
+  for (const Range r : {span(q, tbytes), span(k, tbytes), span(v, tbytes), span(o, tbytes),
+                        span(dO, tbytes), span(lse, rows * 4), span(dq, tbytes),
+                        span(dk, tbytes), span(dv, tbytes)})
+    if (overlap(rw, r)) return FA_ERR_ALIAS;
 
   char* ws = static_cast<char*>(workspace);
-  fa::BwdParams p;
+  BwdParams p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.dO = dO;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.blockmask = blockmask;
@@ -241,12 +260,12 @@ int bwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if ((st = set_dropout(dropout_p, seed, offset, &p.drop_on, &p.drop_t, &p.drop_rp, &p.seed_lo,
                         &p.seed_hi, &p.drop_offset)) != FA_OK)
     return st;
-  if (fa::launch_bwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_bwd(p, d, dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FA_ERR_LAUNCH;
   return FA_OK;
 }
 
-}  // namespace
+}  // namespace fa
 
 extern "C" {
 
@@ -255,7 +274,7 @@ int fa_bwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa
                   int B, int H, int N, int d, float scale, int causal,
                   const uint8_t* blockmask, const int32_t* kv_len, int window_left,
                   int window_right, void* workspace, void* stream) {
-  return bwd_impl(fa::kBf16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
+  return fa::bwd_entry(fa::kBf16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
                   blockmask, kv_len, window_left, window_right, 0.f, 0, 0, workspace, stream);
 }
 
@@ -264,7 +283,7 @@ int fa_bwd_f16(const fa_f16* q, const fa_f16* k, const fa_f16* v, const fa_f16* 
                int H, int N, int d, float scale, int causal, const uint8_t* blockmask,
                const int32_t* kv_len, int window_left, int window_right, void* workspace,
                void* stream) {
-  return bwd_impl(fa::kF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
+  return fa::bwd_entry(fa::kF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
                   blockmask, kv_len, window_left, window_right, 0.f, 0, 0, workspace, stream);
 }
 
@@ -296,7 +315,7 @@ int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const
                    const int32_t* kv_len, int window_left, int window_right, float dropout_p,
                    uint64_t seed, uint32_t offset, void* workspace, void* stream) {
   if (!dtype_ok(dtype)) return FA_ERR_DTYPE;
-  return bwd_impl(dtype, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  return fa::bwd_entry(dtype, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                   static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse,
                   static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
                   static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d, scale,

@@ -214,3 +214,70 @@ def test_fp8_entry_point_validates(lib):
     assert call(w=p[2]) == 7                                   # workspace overlaps v
     assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 100, 128) == 2 * 128 * 128  # N -> 128
     assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 100, 96) == 0
+
+
+# ---------------------------------------------- the Python binding's argument checks
+# Host tensors are used; dtype and size are checked before the device, so every call
+# below raises before anything reaches the library.
+
+def _bf(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _fwd_py(**over):
+    import torch
+    B, H, N, d = 2, 1, 200, 64
+    a = dict(q=_bf(B, H, N, d), k=_bf(B, H, N, d), v=_bf(B, H, N, d), o=_bf(B, H, N, d),
+             lse=torch.zeros((B, H, N)), blockmask=None, kv_len=None)
+    a.update(over)
+    fa.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], B, H, N, d, 0.125, 1,
+                     a["blockmask"], a["kv_len"], -1, -1, stream=0)
+
+
+@pytest.mark.parametrize("over,msg", [
+    ({"kv_len": "int64"}, "dtype"),
+    ({"kv_len": "short"}, "elements"),
+    ({"blockmask": "small"}, "elements"),
+    ({"blockmask": "int32"}, "dtype"),
+    ({"k": "longer"}, "elements"),
+    ({"v": "f16"}, "dtype"),
+    ({"lse": "f64"}, "dtype"),
+    ({"o": "short"}, "elements"),
+    ({}, "GPU tensor"),
+])
+def test_python_binding_checks_dtype_and_size(over, msg):
+    import torch
+    make = {"int64": lambda n: torch.tensor([200, 100]),
+            "short": lambda n: torch.zeros(1, dtype=torch.int32) if n == "kv_len"
+            else _bf(2, 1, 199, 64),
+            "small": lambda n: torch.ones((1, 1), dtype=torch.uint8),
+            "int32": lambda n: torch.ones((2, 2), dtype=torch.int32),
+            "longer": lambda n: _bf(2, 1, 256, 64),
+            "f16": lambda n: _bf(2, 1, 200, 64, dtype=torch.float16),
+            "f64": lambda n: torch.zeros((2, 1, 200), dtype=torch.float64)}
+    args = {name: make[kind](name) for name, kind in over.items()}
+    with pytest.raises(ValueError, match=msg):
+        _fwd_py(**args)
+
+
+def test_python_binding_checks_backward_workspace_and_fp8_types():
+    import torch
+    B, H, N, d = 1, 2, 64, 128
+    t = [_bf(B, H, N, d) for _ in range(8)]
+    lse = torch.zeros((B, H, N))
+    small = torch.zeros(fa.fa_bwd_workspace_bytes(B, H, N, d) - 1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="bytes"):
+        fa.fa_bwd_window(t[0], t[1], t[2], t[3], lse, t[4], t[5], t[6], t[7], B, H, N, d,
+                         0.1, 1, None, None, -1, -1, small, stream=0)
+    with pytest.raises(ValueError, match="dtype"):   # fp16 tensors through the bf16 entry
+        fa.fa_bwd_window(*[x.half() for x in t[:4]], lse, *[x.half() for x in t[4:]], B, H, N,
+                         d, 0.1, 1, None, None, -1, -1, small, stream=0)
+    q8 = torch.zeros((B, H, N, d), dtype=torch.uint8)
+    ws = torch.zeros(fa.fa_fwd_fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="dtype"):   # O of the FP8 forward is bf16
+        fa.fa_fwd_fp8(q8, q8, q8, torch.zeros((B, H, N, d)), lse, B, H, N, d, 0.1, 1.0, 1.0,
+                      1.0, 1, None, None, -1, -1, ws, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        fa.fa_fwd_fp8(t[0], q8, q8, t[1], lse, B, H, N, d, 0.1, 1.0, 1.0, 1.0, 1, None, None,
+                      -1, -1, ws, stream=0)
