@@ -193,7 +193,7 @@ def fp8_cpu_baseline(x, heads=2):
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(sel)} of {wl.B * wl.H} heads of {wl.name} (N={wl.N}, d={wl.d}): "
                       f"fp64 FP8-quantised forward with S and P materialised, numpy/OpenBLAS, "
                       f"{dt:.1f} s wall"}
@@ -217,6 +217,7 @@ def fp8_main(args, torch, wl, x):
                    "causal": wl.causal, "mask": wl.mask, "window": wl.window,
                    "scale": wl.scale, "descale": list(x.descale), "allowed_pairs": pairs},
         "fwd_tflops": round(tf_fwd, 2), "fwd_ms": round(ms_fwd, 4),
+        "timing_ms": {"fwd": timing_record(ms_fwd)},
         "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_FP8_PEAK_TFLOPS, 2),
         "roofline": {"kernel": f"{k_fwd} + vt_fp8_kernel<{wl.d}> (whole forward)",
                      "bound": "mfma", "achieved": round(tf_fwd, 2),
@@ -224,6 +225,11 @@ def fp8_main(args, torch, wl, x):
                      "frac": round(tf_fwd / MFMA_FP8_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name, "fp8_kernel", [k_fwd])},
     }
+    peak = mfma_peak_record("fp8")
+    rec["mfma_peak"] = peak
+    if "tflops" in peak:
+        rec["fwd_pct_measured_mfma_peak"] = round(100 * tf_fwd / peak["tflops"], 2)
+        rec["roofline"]["frac_of_measured_peak"] = round(tf_fwd / peak["tflops"], 4)
     rec["device"] = None if args.no_device_sample else device_sample(torch, buf.fwd)
     rec["context"] = {"note": "the pages' figures on their own hardware; context only",
                       "items": PAGE_CONTEXT}
@@ -284,19 +290,45 @@ def device_sample(torch, fn, seconds=5.0):
         return None
 
 
+class Timing(float):
+    """Mean milliseconds per call (the float value), with the median and minimum of the
+    per-call times as attributes."""
+
+    def __new__(cls, mean, median, minimum):
+        t = super().__new__(cls, mean)
+        t.median, t.min = median, minimum
+        return t
+
+
 def time_loop(torch, fn, steps, warmup):
-    """Mean milliseconds per call, HIP events on the stream the kernels run on."""
+    """Milliseconds per call, HIP events on the stream the kernels run on: ``steps`` calls
+    back to back with an event between each two, no synchronisation inside the timed
+    region. The mean is first-to-last event over ``steps``."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(s)
+    for i in range(steps):
         fn()
-    e1.record(s)
+        ev[i + 1].record(s)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return Timing(ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2], per[0])
+
+
+def timing_record(t):
+    return {"mean": round(float(t), 4), "median": round(t.median, 4), "min": round(t.min, 4)}
+
+
+def mfma_peak_record(dtype):
+    """The matrix-core probe's sustained rate (bf16 or fp8), or None if it cannot run."""
+    try:
+        from exact_io_aware_46_amd import mfma_peak
+        return mfma_peak.measure(dtype)
+    except Exception as e:  # noqa: BLE001 -- a missing probe leaves only the spec fraction
+        return {"error": str(e)}
 
 
 def footprint_sweep(torch, base, steps=10, warmup=3):
@@ -392,7 +424,7 @@ def cpu_baseline(x, heads=4):
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(sel)} of {wl.B * wl.H} heads of {wl.name} (N={wl.N}, d={wl.d}): "
                       f"fp64 forward+backward with S and P materialised, numpy/OpenBLAS, "
                       f"{dt:.1f} s wall"}
@@ -459,6 +491,10 @@ def main():
         "fwd_pct_mfma_peak": round(100 * tf_fwd / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_bwd_pct_mfma_peak": round(100 * tf_step / MFMA_BF16_PEAK_TFLOPS, 2),
         "bwd_ms": round(ms_bwd, 4), "bwd_preprocess_ms": round(ms_pre, 4),
+        "timing_ms": {"step": timing_record(ms_step), "fwd": timing_record(ms_fwd),
+                      "bwd": timing_record(ms_bwd), "bwd_preprocess": timing_record(ms_pre)},
+        "fwd_bwd_tflops_at_median": round((fl_fwd + fl_bwd) / (ms_step.median * 1e-3) / 1e12, 2),
+        "fwd_tflops_at_median": round(fl_fwd / (ms_fwd.median * 1e-3) / 1e12, 2),
         "roofline": {"kernel": f"{k_dkdv} + {k_dq} (backward minus its preprocess)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -470,6 +506,14 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf_fwd / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(wl.name, "fwd_kernel", [k_fwd])},
     }
+    peak = mfma_peak_record("bf16")
+    rec["mfma_peak"] = peak
+    if "tflops" in peak:
+        m = peak["tflops"]
+        rec["fwd_pct_measured_mfma_peak"] = round(100 * tf_fwd / m, 2)
+        rec["fwd_bwd_pct_measured_mfma_peak"] = round(100 * tf_step / m, 2)
+        rec["roofline"]["frac_of_measured_peak"] = round(tf_bwd_main / m, 4)
+        rec["roofline_fwd"]["frac_of_measured_peak"] = round(tf_fwd / m, 4)
     rec["device"] = None if args.no_device_sample else device_sample(torch, buf.step)
     rec["context"] = {"note": "the pages' figures on their own hardware; context only",
                       "source": "IO感知计算如何重塑Transformer内存优化技术格局 (bxzpzcl.cn), "

@@ -3,6 +3,7 @@
     python -m exact_io_aware_46_amd.build
 
 Objects go to exact_io_aware_46_amd/_build/, the library to exact_io_aware_46_amd/libfa.so.
+The bench's matrix-core probe (csrc/mfma_peak.hip) is built beside it as libmfma_peak.so.
 """
 from __future__ import annotations
 
@@ -16,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+PEAK_LIB = os.path.join(PKG, "libmfma_peak.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
 ARCH = "gfx950"
 
@@ -34,19 +36,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-           f"-Wl,--version-script={os.path.join(CSRC, 'libfa.map')}"]
+def _link(objs, out, extra=()):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *extra]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + ["mfma_peak.hip"]))
+    _link(objs[:-1], LIB, [f"-Wl,--version-script={os.path.join(CSRC, 'libfa.map')}"])
+    _link(objs[-1:], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 
