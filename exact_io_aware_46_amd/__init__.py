@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED_D",
                 4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_LAUNCH", 7: "FA_ERR_ALIAS",
-                8: "FA_ERR_DROPOUT", 9: "FA_ERR_DTYPE"}
+                8: "FA_ERR_DROPOUT", 9: "FA_ERR_DTYPE", 10: "FA_ERR_SCRATCH"}
 DTYPE_BF16, DTYPE_F16 = 0, 1
 
 _lib = None
@@ -48,6 +48,8 @@ _SIGNATURES = {
                             _U64, _U32, _P]),
     "fa_bwd_dropout": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
                             _P, _I, _I, _F, _U64, _U32, _P, _P]),
+    "fa_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
+                            _P, _I, _I, _F, _U64, _U32, _P]),
     "fa_fwd_fp8_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _I, _P, _P, _I, _I,
                         _P, _P]),
@@ -279,6 +281,17 @@ def fa_bwd_dropout(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, ca
           int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), int(window_left),
           int(window_right), float(dropout_p), int(seed), int(offset),
           a.workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d)), _stream_ptr(stream))
+
+
+def fa_bwd_noalloc(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal=0,
+                   blockmask=None, kv_len=None, window_left=-1, window_right=-1,
+                   dropout_p=0.0, seed=0, offset=0, stream=None):
+    """fa_bwd_dropout with the library's static device scratch as its workspace."""
+    a = _Args(B, H, N, d)
+    _call(a, "fa_bwd_noalloc", int(dtype),
+          *a.bwd(_kind(dtype), q, k, v, o, lse, dO, dq, dk, dv), B, H, N, d, float(scale),
+          int(bool(causal)), a.blockmask(blockmask), a.kv_len(kv_len), int(window_left),
+          int(window_right), float(dropout_p), int(seed), int(offset), _stream_ptr(stream))
 
 
 def fa_fwd_fp8_workspace_bytes(B, H, N, d):

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "../../include/fa.h"
+#include "fa_entry.h"
 #include "fa_internal.h"
 
 namespace {
@@ -80,6 +81,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
     case FA_ERR_DTYPE: return "unknown element type (0 = bfloat16, 1 = fp16)";
+    case FA_ERR_SCRATCH: return "problem too large for fa_bwd_noalloc's static scratch (B * H * N above 2^22 rows)";
     default: return "unknown status";
   }
 }

@@ -85,18 +85,6 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
                                  float* delta, float* lse2, int rows, int d, float dsign,
                                  int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream);
-// Backward entry shared by the C-ABI front ends: bwd_check validates every argument but
-// the workspace (FA_OK or a fa_status); bwd_entry validates everything, lays out the
-// workspace and launches.
-int bwd_check(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-              const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-              int B, int H, int N, int d, float scale, const int32_t* kv_len, float dropout_p);
-int bwd_entry(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-              const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
-              uint16_t* dk, uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
-              const uint8_t* blockmask, const int32_t* kv_len, int window_left,
-              int window_right, float dropout_p, uint64_t seed, uint32_t offset,
-              void* workspace, void* stream);
 // Transposes v into vt (p.vt), then runs the FP8 forward.
 hipError_t launch_fwd_fp8(const Fp8Params& p, const uint8_t* v, uint8_t* vt, int d,
                           hipStream_t stream);

@@ -79,7 +79,8 @@ enum fa_status {
   FA_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch            */
   FA_ERR_ALIAS = 7,          /* an output buffer overlaps an input or another output */
   FA_ERR_DROPOUT = 8,        /* dropout probability not in [0, 1)                    */
-  FA_ERR_DTYPE = 9           /* element type other than 0 (bfloat16) or 1 (fp16)     */
+  FA_ERR_DTYPE = 9,          /* element type other than 0 (bfloat16) or 1 (fp16)     */
+  FA_ERR_SCRATCH = 10        /* fa_bwd_noalloc: B * H * N above its static scratch     */
 };
 
 /* Forward. Writes O [B][H][N][d] (bf16) and LSE [B][H][N] (fp32, natural log).
@@ -202,6 +203,23 @@ int fa_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, fa_bf16* o,
                int B, int H, int N, int d, float scale, float descale_q, float descale_k,
                float descale_v, int causal, const uint8_t* blockmask, const int32_t* kv_len,
                int window_left, int window_right, void* workspace, void* stream);
+
+/* Backward without a workspace argument, for callers that cannot allocate device memory
+ * around the call (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Arguments, layout, semantics and results as fa_bwd_dropout (dtype, every
+ * mask, dropout_p = 0 for none), bitwise; it allocates nothing and calls no allocating
+ * routine. Its workspace is a static device array of 32 MiB in the library, one copy per
+ * GPU, held until the process ends: B * H * N must be at most 4,194,304 (2^22) rows, else
+ * FA_ERR_SCRATCH and nothing is launched. It uses the copy of the current device (the
+ * stream must belong to it); the first call on a device looks the copy up. Calls on one GPU
+ * share the array, so calls that overlap on one GPU (different streams or threads) race;
+ * calls on one stream are ordered and safe. Errors as fa_bwd_dropout, plus FA_ERR_SCRATCH,
+ * and FA_ERR_LAUNCH if the device or its copy of the array cannot be found. */
+int fa_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int N, int d, float scale, int causal, const uint8_t* blockmask,
+                   const int32_t* kv_len, int window_left, int window_right, float dropout_p,
+                   uint64_t seed, uint32_t offset, void* stream);
 
 /* Static description of a status code. */
 const char* fa_strerror(int status);

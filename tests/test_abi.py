@@ -38,7 +38,8 @@ def lib():
 def test_library_exports_exactly_the_header(lib):
     decl = declared_functions()
     assert decl == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_ex", "fa_bwd_f16",
-                    "fa_bwd_preprocess", "fa_bwd_preprocess_f16", "fa_bwd_window",
+                    "fa_bwd_noalloc", "fa_bwd_preprocess", "fa_bwd_preprocess_f16",
+                    "fa_bwd_window",
                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_dropout", "fa_fwd_ex",
                     "fa_fwd_f16", "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes", "fa_fwd_window",
                     "fa_strerror"]
@@ -48,7 +49,7 @@ def test_library_exports_exactly_the_header(lib):
 
 
 def test_strerror(lib):
-    for st in range(10):
+    for st in range(11):
         assert len(fa.strerror(st)) > 0
     assert fa.strerror(99) == "unknown status"
 
@@ -281,3 +282,22 @@ def test_python_binding_checks_backward_workspace_and_fp8_types():
     with pytest.raises(ValueError, match="dtype"):
         fa.fa_fwd_fp8(t[0], q8, q8, t[1], lse, B, H, N, d, 0.1, 1.0, 1.0, 1.0, 1, None, None,
                       -1, -1, ws, stream=0)
+
+
+def test_noalloc_backward_validates_and_rejects_sizes_past_its_scratch(lib):
+    # Same checks as fa_bwd_dropout (no workspace argument), then the static scratch limit
+    # of 2^22 rows; all before any HIP call.
+    p = ptrs(9)
+
+    def call(B=1, H=1, N=64, d=64, dt=0, pd=0.0, q=p[0]):
+        return lib.fa_bwd_noalloc(dt, q, p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], B, H,
+                                  N, d, 0.125, 1, None, None, -1, -1, pd, 0, 0, None)
+    assert call(q=None) == 1                     # FA_ERR_NULL
+    assert call(N=0) == 2                        # FA_ERR_SHAPE
+    assert call(d=12) == 3                       # FA_ERR_UNSUPPORTED_D
+    assert call(q=p[0] + 2) == 4                 # FA_ERR_ALIGN
+    assert call(pd=1.0) == 8                     # FA_ERR_DROPOUT
+    assert call(dt=3) == 9                       # FA_ERR_DTYPE
+    assert call(B=2, H=64, N=32769, d=8) == 10   # FA_ERR_SCRATCH: 4,194,432 rows
+    assert call(B=1, H=128, N=32769, d=8) == 10
+    assert fa.STATUS_NAMES[10] == "FA_ERR_SCRATCH"
