@@ -913,7 +913,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
       // Exponent of P; a masked element's is -inf (P = 0 for either sign of the scale).
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = s[i] * sc - lq;
-      if (MASKED && need_mask) {
+      if (MASKED && need_mask) [[unlikely]] {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + acc_row(i, hi);
