@@ -210,11 +210,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
         }
     }
 
-    float mx = -kInf;
+    // Row maximum as four independent chains (a single chain would serialise every
+    // max on the previous one's result).
+    float mq[4] = {-kInf, -kInf, -kInf, -kInf};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = 0; i < 16; ++i) mq[i & 3] = fmaxf(mq[i & 3], s[kb][i]);
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = xhalf_max(mx) * sc;
     const bool up = mx > m_run + 8.f;
     if (__builtin_amdgcn_ballot_w64(up)) {

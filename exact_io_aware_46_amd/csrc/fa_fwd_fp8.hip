@@ -246,11 +246,14 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
         }
     }
 
-    float mx = -kInf;
+    // Row maximum as four independent chains (a single chain would serialise every
+    // max on the previous one's result).
+    float mq[4] = {-kInf, -kInf, -kInf, -kInf};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      for (int i = 0; i < 16; ++i) mq[i & 3] = fmaxf(mq[i & 3], s[kb][i]);
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = xhalf_max(mx) * p.sc;
     const bool up = mx > m_run + 2.8f;
     if (__builtin_amdgcn_ballot_w64(up)) {
