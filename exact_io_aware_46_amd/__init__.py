@@ -91,11 +91,18 @@ def strerror(status: int) -> str:
 # the library asks for), then on the GPU and contiguous. A raw integer is passed through
 # as a device address without checks. Violations raise ValueError and nothing is called.
 
+_DTYPES = None
+
+
 def _dtypes(kind):
-    import torch
-    return {"bf16": (torch.bfloat16,), "f16": (torch.float16,), "f32": (torch.float32,),
-            "i32": (torch.int32,), "mask": (torch.uint8, torch.bool),
-            "fp8": (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))}[kind]
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+        _DTYPES = {"bf16": (torch.bfloat16,), "f16": (torch.float16,),
+                   "f32": (torch.float32,), "i32": (torch.int32,),
+                   "mask": (torch.uint8, torch.bool),
+                   "fp8": (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))}
+    return _DTYPES[kind]
 
 
 class _Args:
@@ -118,20 +125,20 @@ class _Args:
         if kind is not None and t.dtype not in _dtypes(kind):
             raise ValueError(f"{name} must have dtype "
                              f"{' or '.join(map(str, _dtypes(kind)))}, got {t.dtype}")
-        if numel is not None and t.numel() != numel:
-            raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
-        if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
-            raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, "
-                             f"needs {min_bytes}")
-        self._seen.append((name, t))
+        n = t.numel()
+        if numel is not None and n != numel:
+            raise ValueError(f"{name} has {n} elements, expected {numel}")
+        if min_bytes is not None and n * t.element_size() < min_bytes:
+            raise ValueError(f"{name} has {n * t.element_size()} bytes, needs {min_bytes}")
+        self._seen.append(t)
         return t.data_ptr()
 
     def ready(self):
-        for name, t in self._seen:
-            if not t.is_cuda:
-                raise ValueError(f"{name} must be a GPU tensor")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
+        for t in self._seen:
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError(f"{'a tensor on the host' if not t.is_cuda else 'a non-contiguous tensor'}"
+                                 f" (shape {tuple(t.shape)}, {t.dtype}): every tensor must be a "
+                                 "contiguous GPU tensor")
 
     def fwd(self, kind, q, k, v, o, lse):
         return [self.add(q, "q", kind, self.t), self.add(k, "k", kind, self.t),
