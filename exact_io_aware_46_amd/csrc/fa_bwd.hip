@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 
   auto next_q = [&](int qt) {
     if (p.blockmask)
-      while (qt < qt_end && !p.blockmask[(size_t)((qt * BQ) >> 7) * nb + (k0 >> 7)]) ++qt;
+      while (qt < qt_end && !bm_keep(p.blockmask + (size_t)((qt * BQ) >> 7) * nb, k0 >> 7)) ++qt;
     return qt;
   };
   // Query tile qt -> stage: Q and dO rows (row-major, swizzled), log2-scaled LSE and D.
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
 
   auto next_q = [&](int qt) {
     if (p.blockmask)
-      while (qt < qt_end && !p.blockmask[(size_t)((qt * BQ) >> 7) * nb + (k0 >> 7)]) ++qt;
+      while (qt < qt_end && !bm_keep(p.blockmask + (size_t)((qt * BQ) >> 7) * nb, k0 >> 7)) ++qt;
     return qt;
   };
   // Query tile qt -> stage (rows past N fetch row N-1; masked later).
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   // Next key tile at or after kt that either query block keeps (all without a table).
   auto next_tile = [&](int kt) {
     if (bm0)
-      while (kt < nkt && !bm0[(kt * BC) >> 7] && !bm1[(kt * BC) >> 7]) ++kt;
+      while (kt < nkt && !bm_keep(bm0, (kt * BC) >> 7) && !bm_keep(bm1, (kt * BC) >> 7)) ++kt;
     return kt;
   };
   // Key tile kt -> stage (K and V rows; rows at or past klim fetch row klim-1, masked).
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
-    if (bmw && !bmw[k0 >> 7]) return;  // block masked for this wave
+    if (bmw && !bm_keep(bmw, k0 >> 7)) return;  // block masked for this wave
     const bool need_mask = k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim;
     if constexpr (D == 64) {
       if (need_mask) tile(std::true_type{}, k0, sK, sV, true);
@@ -1042,6 +1042,16 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
   // its key tiles can hold 128 keys (one barrier and copy round per 128 keys; 128 KB of
   // LDS); the 64 and 256 layouts take tiles of 64.
   constexpr int BCQ = D == 128 ? 128 : 64;
+  if constexpr (D == 64 && !DROP) {
+    // With a block table, four-wave workgroups of 128 queries (one table row each), as in
+    // the forward: no wave idles through key tiles that only another query block keeps.
+    if (p.blockmask) {
+      const dim3 g_q4((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, 4>), g_q4, dim3(256), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
                      stream, p);
   return hipGetLastError();

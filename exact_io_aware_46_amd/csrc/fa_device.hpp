@@ -301,4 +301,18 @@ __device__ __forceinline__ int right_limit(int causal, int wr) {
 }
 __device__ __forceinline__ int left_limit(int wl) { return wl >= 0 ? wl : kUnlimited; }
 
+// Entry `blk` of a block-table row (nonzero: keep the 128 x 128 block), read by the scalar
+// unit. Every caller's address is uniform across the wave. A vector byte load here would
+// share the vector memory counter with the tile copies, and the wait for its result would
+// also wait for the copy of the next tile issued just before it, leaving the copy's whole
+// latency exposed on every tile; a scalar load has its own counter. Scalar loads read
+// aligned dwords: the dword that holds the byte lies in the same page as the byte, so the
+// read stays within the table's pages. The table is read-only while any kernel runs.
+__device__ __forceinline__ bool bm_keep(const uint8_t* row, int blk) {
+  typedef __attribute__((address_space(4))) const uint32_t const_u32;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row) + (uintptr_t)blk;
+  const uint32_t w = *reinterpret_cast<const_u32*>(a & ~uintptr_t(3));
+  return ((w >> (8 * (a & 3))) & 0xffu) != 0;
+}
+
 }  // namespace fa

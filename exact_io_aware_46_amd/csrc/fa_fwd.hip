@@ -39,7 +39,8 @@ namespace {
 // NW: waves per workgroup (8, two per SIMD; 4 for d = 256, whose accumulators need the
 // registers of one wave per SIMD).
 template <typename T, int D, int BC, bool DROP, bool PAD, int DC, int NW>
-__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 4 : 1))) void fwd_kernel(FwdParams p) {
   constexpr int BR = 32 * NW;       // queries per workgroup (NW waves x 32)
   constexpr int NS = DC / 16;       // contraction steps of the score MFMA
   constexpr int KB = BC / 32;       // 32-key blocks per key tile
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   // Next key tile at or after kt that either query block keeps (all without a table).
   auto next_tile = [&](int kt) {
     if (bm0)
-      while (kt < nkt && !bm0[(kt * BC) >> 7] && !bm1[(kt * BC) >> 7]) ++kt;
+      while (kt < nkt && !bm_keep(bm0, (kt * BC) >> 7) && !bm_keep(bm1, (kt * BC) >> 7)) ++kt;
     return kt;
   };
   // Asynchronous copy of key tile kt into a stage: every lane moves 16 bytes straight
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;  // nothing allowed
-    if (bmw && !bmw[k0 >> 7]) return;                   // block masked for this wave
+    if (bmw && !bm_keep(bmw, k0 >> 7)) return;                   // block masked for this wave
 
     f32x16 s[KB];
 #pragma unroll
@@ -343,7 +344,19 @@ hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
   else if (d > 64)
     hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
-  else if (d == 64)
+  else if (!DROP && p.blockmask) {
+    // 64-wide layout with a block table: four-wave workgroups of 128 queries, one row of
+    // the table each. The two query blocks of an eight-wave workgroup copy the union of
+    // the key blocks either keeps, and each wave idles through the tiles that only the
+    // other block keeps. Four waves per SIMD, as with eight-wave workgroups.
+    const dim3 grid4((unsigned)((p.N + 127) / 128) * bh);
+    if (d == 64)
+      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, false, 64, 4>), grid4, dim3(256), 0, stream, p);
+    else if (d == 32)
+      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, true, 32, 4>), grid4, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, true, 64, 4>), grid4, dim3(256), 0, stream, p);
+  } else if (d == 64)
     hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64, 8>), grid, dim3(512), 0, stream, p);
   else if (d == 32)
     hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 32, 8>), grid, dim3(512), 0, stream, p);

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 
   auto next_tile = [&](int kt) {
     if (bm0)
-      while (kt < nkt && !bm0[(kt * BC) >> 7] && !bm1[(kt * BC) >> 7]) ++kt;
+      while (kt < nkt && !bm_keep(bm0, (kt * BC) >> 7) && !bm_keep(bm1, (kt * BC) >> 7)) ++kt;
     return kt;
   };
   // Key tile kt -> stage: K rows (rows at or past klim fetch row klim-1, masked later) and
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
-    if (bmw && !bmw[k0 >> 7]) return;
+    if (bmw && !bm_keep(bmw, k0 >> 7)) return;
 
     f32x16 s[2];
 #pragma unroll
