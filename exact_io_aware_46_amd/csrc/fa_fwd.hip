@@ -69,8 +69,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 4 : 1))) void fwd_kernel
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   // Read as uniform: per-wave tests become scalar branches and wave-derived values live in
-  // SGPRs (22 fewer VGPRs at d = 128, 2.5% faster). The backward kernels measured slower
-  // with the same change and keep the plain index.
+  // SGPRs (22 fewer VGPRs at d = 128, 2.5% faster). The dQ kernel reads it the same way;
+  // the dK/dV kernels measured slower with the change and keep the plain index.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
