@@ -500,11 +500,13 @@ def main():
     pad = "false" if wl.d == kd else "true"                    # rows narrower than kd
     dc = wl.d if wl.d in (32, 96) else kd                      # head dim computed on
     nw = 4 if kd == 256 else 8                                 # waves per workgroup
+    # the 64-wide forward and dQ kernels run four-wave workgroups under a block table
+    nwq = 4 if kd == 64 and wl.mask == "block" and dr == "false" else nw
     k_dkdv = (f"bwd_dkdv_rk_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>" if kd == 128
               else f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>")
     bc = 128 if kd == 128 else 64                              # forward and dQ key tile
-    k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nw}>"
-    k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nw}>"
+    k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
+    k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
