@@ -432,8 +432,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------- dK, dV pass, one wave per SIMD (128-wide layout)
 
 // Workgroup = 4 waves = 128 keys of one (b, h); wave w owns keys 32w .. 32w+31 and every
-// query of each 64-query step, as two 32-query blocks. At one wave per SIMD a lane has 512
-// registers, enough to keep the wave's K and V rows in registers as the B operands of
+// query of each 64-query step, as two 32-query blocks. At d = 64 a wave needs under 256
+// registers, and two workgroups share a CU. At d = 128 one wave per SIMD has 512
+// registers per lane, enough to keep the wave's K and V rows in registers as the B operands of
 // S = Q K^T and dP = dO V^T for the whole pass: per step only the Q and dO tiles are read
 // from LDS, once as row operands and once by transpose loads, a third of the LDS bytes per
 // product of the two-wave kernel. With no second wave on the SIMD to cover the softmax,
@@ -445,7 +446,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 // issued a few matrix instructions ahead of their use. The waves own disjoint keys and all
 // columns, so dK and dV are stored with no reduction between waves.
 template <typename T, int D, bool DROP, bool PAD, int DC>
-__global__ __launch_bounds__(256) void bwd_dkdv_rk_kernel(BwdParams p) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_rk_kernel(BwdParams p) {
   constexpr int BKC = 128;            // keys per workgroup
   constexpr int BQ = 64;              // queries per step
   constexpr int NS = DC / 16;         // contraction steps over d
@@ -1029,9 +1031,10 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
   // 1.5% faster than the two-wave kernel at d = 128. d = 96 runs it too, although 0.8%
   // slower there, so that every head dim of the layout sums in the order of d = 128 (its
   // results equal those of d = 128 on zero-padded tensors bit for bit). On the 64-wide
-  // layout a step holds too little matrix work to cover one wave's exponentials, and the
-  // two-wave kernel is 3-10% faster.
-  if constexpr (NW == 8 && D == 128)
+  // layout the same kernel fits 256 registers, so two of its workgroups share a CU and
+  // cover each other's waits: 2-11% faster than the two-wave kernel there. With dropout
+  // it would spill at that budget, and the two-wave kernel stays.
+  if constexpr (NW == 8 && (D == 128 || (D == 64 && !DROP)))
     hipLaunchKernelGGL((bwd_dkdv_rk_kernel<T, D, DROP, PAD, DC>), g_kv, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC, NW>), g_kv, dim3(64 * NW), 0,

@@ -68,3 +68,17 @@ def test_two_wave_kernels_keep_two_waves_per_simd(resources):
     assert eight
     low = {k: v["Occupancy"] for k, v in eight.items() if v.get("Occupancy", 0) < 2}
     assert not low, f"eight-wave kernels below two waves per SIMD: {low}"
+
+
+def test_kernels_that_share_a_cu_keep_their_occupancy(resources):
+    # On the 64-wide layout: the four-wave forward (block tables) runs four waves per SIMD,
+    # like the eight-wave one; the four-wave dQ kernel and the one-wave-per-SIMD dK/dV
+    # kernel fit two workgroups per CU.
+    want = {r"fwd_kernel.*ELi64ELi64ELb0E.*Li4EEEv": 4,
+            r"bwd_dq_kernel.*ELi64ELi64ELb0E.*Li4EEEv": 2,
+            r"bwd_dkdv_rk_kernel.*ELi64ELb0E": 2}
+    for pat, occ in want.items():
+        found = {k: v.get("Occupancy", 0) for k, v in resources.items() if re.search(pat, k)}
+        assert found, pat
+        low = {k: o for k, o in found.items() if o < occ}
+        assert not low, f"below {occ} waves per SIMD: {low}"
