@@ -508,7 +508,8 @@ def main():
     nw = 4 if kd == 256 else 8                                 # waves per workgroup
     # the 64-wide forward and dQ kernels run four-wave workgroups under a block table
     nwq = 4 if kd == 64 and wl.mask == "block" and dr == "false" else nw
-    k_dkdv = (f"bwd_dkdv_rk_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>" if kd == 128
+    rk = kd == 128 or (kd == 64 and dr == "false")             # one-wave dK/dV kernel
+    k_dkdv = (f"bwd_dkdv_rk_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>" if rk
               else f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>")
     bc = 128 if kd == 128 else 64                              # forward and dQ key tile
     k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
