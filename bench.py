@@ -511,8 +511,9 @@ def main():
     rk = kd == 128 or (kd == 64 and dr == "false")             # one-wave dK/dV kernel
     k_dkdv = (f"bwd_dkdv_rk_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>" if rk
               else f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>")
-    bc = 128 if kd == 128 else 64                              # forward and dQ key tile
-    k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
+    bc = 128 if kd == 128 else 64                              # forward key tile
+    bcq = 128 if kd <= 128 else 64                             # dQ key tile
+    k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bcq}, {dr}, {pad}, {dc}, {nwq}>"
     k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -1041,10 +1041,10 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
                        stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // The dQ pass keeps one 32-key block of S and dP live at a time, so on the 128 layout
-  // its key tiles can hold 128 keys (one barrier and copy round per 128 keys; 128 KB of
-  // LDS); the 64 and 256 layouts take tiles of 64.
-  constexpr int BCQ = D == 128 ? 128 : 64;
+  // The dQ pass keeps one 32-key block of S and dP live at a time, so its key tiles can
+  // hold 128 keys (one barrier and copy round per 128 keys; 128 KB of LDS on the 128
+  // layout, 64 KB on the 64 one) at no register cost; the 256 layout's LDS holds 64.
+  constexpr int BCQ = D <= 128 ? 128 : 64;
   if constexpr (D == 64 && !DROP) {
     // With a block table, four-wave workgroups of 128 queries (one table row each), as in
     // the forward: no wave idles through key tiles that only another query block keeps.

@@ -75,7 +75,7 @@ def test_kernels_that_share_a_cu_keep_their_occupancy(resources):
     # like the eight-wave one; the four-wave dQ kernel and the one-wave-per-SIMD dK/dV
     # kernel fit two workgroups per CU.
     want = {r"fwd_kernel.*ELi64ELi64ELb0E.*Li4EEEv": 4,
-            r"bwd_dq_kernel.*ELi64ELi64ELb0E.*Li4EEEv": 2,
+            r"bwd_dq_kernel.*ELi64ELi128ELb0E.*Li4EEEv": 2,
             r"bwd_dkdv_rk_kernel.*ELi64ELb0E": 2}
     for pat, occ in want.items():
         found = {k: v.get("Occupancy", 0) for k, v in resources.items() if re.search(pat, k)}
