@@ -37,10 +37,12 @@
  *   q, k, v, o, dO, dq, dk, dv: contiguous [B][H][N][d] bfloat16 or fp16 (raw bits,
  *     uint16), DEVICE pointers, 16-byte aligned.
  *   lse, delta: contiguous [B][H][N] float32, DEVICE pointers, 4-byte aligned.
- *   blockmask, kv_len: DEVICE pointers or NULL (NULL = mask not used).
+ *   blockmask, kv_len: DEVICE pointers or NULL (NULL = mask not used); blockmask at any
+ *     byte alignment, kv_len 4-byte aligned.
  *   workspace: DEVICE pointer, 256-byte aligned, at least fa_bwd_workspace_bytes() bytes.
  *   The caller allocates and frees everything; the library allocates nothing and keeps no
- *   global mutable state. Outputs must not alias inputs or each other.
+ *   global mutable state (except the scratch array of fa_bwd_noalloc, described there).
+ *   Outputs must not alias inputs or each other.
  *   stream: a hipStream_t (NULL = the default stream). All work is enqueued asynchronously
  *   on it; inputs must stay valid and unmodified until the stream has run the work.
  *   Supported head dims: d a multiple of 8 from 8 to 256 (the FP8 forward: 64 and 128).

@@ -142,6 +142,46 @@ def test_all_ones_block_mask_is_bitwise_dense(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_block_table_at_odd_addresses_is_bitwise_the_aligned_one(d):
+    """The kernels read the block table through the scalar unit, a dword at a time, and
+    pick the byte out of it. A table that starts at byte 1, 2 or 3 of a dword (and its
+    rows, N = 300 giving 3-byte rows, at every alignment) must give every output bit for
+    bit as the same table at an aligned address."""
+    import exact_io_aware_46_amd as fa
+    N = 300
+    q, k, v, do = (to_dev(x) for x in inp.custom_inputs(2, 2, N, d, seed=231 + d))
+    table = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    say(f"[bitexact] block table at odd addresses d={d}")
+    aligned = torch.from_numpy(table).cuda()
+
+    def run(bm):
+        o, lse = fa.forward(q, k, v, 0.13, True, bm)
+        grads = fa.backward(q, k, v, o, lse, do, 0.13, True, bm)
+        torch.cuda.synchronize()
+        return (o, lse, *grads)
+
+    ref = run(aligned)
+    buf = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    for off in (1, 2, 3, 55):
+        bm = buf[off:off + 9].view(3, 3)
+        bm.copy_(aligned)
+        assert bm.data_ptr() % 4 == off % 4
+        for a, b in zip(run(bm), ref):
+            it = torch.int16 if a.element_size() == 2 else torch.int32
+            assert torch.equal(a.view(it), b.view(it)), f"offset {off}"
+    q8, k8, v8, desc = _fp8_inputs(2, 2, N, d, seed=233 + d)
+    q8, k8, v8 = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8, v8))
+    o_ref, l_ref = fa.forward_fp8(q8, k8, v8, 0.09, desc, True, aligned)
+    for off in (1, 3):
+        bm = buf[off:off + 9].view(3, 3)
+        bm.copy_(aligned)
+        o, l = fa.forward_fp8(q8, k8, v8, 0.09, desc, True, bm)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"fp8 offset {off}"
+        assert torch.equal(l, l_ref), f"fp8 offset {off}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_padding_poison_is_bitwise_invisible(d):
     """Keys past kv_len filled with NaN change nothing (every output bitwise)."""
     N = 300
