@@ -340,7 +340,7 @@ int fa_bwd(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, const fa_bf16* 
 namespace {
 
 size_t fp8_vt_bytes(int B, int H, int N, int d) {
-  return (size_t)B * H * d * round_up((size_t)N, 64);
+  return (size_t)B * H * d * round_up((size_t)N, 128);
 }
 
 }  // namespace
@@ -381,7 +381,7 @@ int fa_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, fa_bf16* o,
   p.blockmask = blockmask;
   p.kv_len = kv_len;
   p.B = B; p.H = H; p.N = N;
-  p.Np = (int)round_up((size_t)N, 64);
+  p.Np = (int)round_up((size_t)N, 128);
   p.sc = std::fabs(scale) * descale_q * descale_k * fa::kLog2eHost;
   p.qsign = scale < 0.f ? 0x80808080u : 0u;
   p.descale_v = descale_v;

@@ -53,14 +53,14 @@ __device__ __forceinline__ int pi_row(int r) {
 //   pi(0..15) or pi(16..31) (+32): for D = 128 the even and the odd ones need distinct
 //   swizzles (row parity picks the bank half), for D = 64 the four rows of each residue
 //   mod 4.
-//   V^T tiles, 64-byte rows (4 chunks): rows 16k .. 16k+15; the four rows of each residue
-//   mod 4 need distinct swizzles.
+//   V^T tiles, 128-byte rows (8 chunks): rows 16k .. 16k+15; the eight rows of each parity
+//   need distinct swizzles.
 template <int D>
 __device__ __forceinline__ int swz_k8(int r) {
   if constexpr (D == 128) return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
   else return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
 }
-__device__ __forceinline__ int swz_v8(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_v8(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
@@ -103,11 +103,12 @@ __global__ __launch_bounds__(256) void vt_fp8_kernel(const uint8_t* __restrict__
 template <int D>
 __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int BR = 256;            // queries per workgroup (8 waves x 32)
-  constexpr int BC = 64;             // keys per tile
+  constexpr int BC = 128;            // keys per tile
+  constexpr int KB = BC / 32;        // 32-key score blocks per tile
   constexpr int NS = D / 64;         // contraction steps of the score MFMA
   constexpr int DB = D / 32;         // 32-wide column blocks of O
   constexpr int KT = BC * D;         // bytes of a K tile (row-major, D-byte rows)
-  constexpr int VT = D * BC;         // bytes of a V^T tile (row-major, 64-byte rows)
+  constexpr int VT = D * BC;         // bytes of a V^T tile (row-major, 128-byte rows)
   constexpr int KLOADS = KT / 1024;  // 1 KB wave-wide copies per K tile (and per V^T tile)
   __shared__ __attribute__((aligned(1024))) char sK0[KT];
   __shared__ __attribute__((aligned(1024))) char sV0[VT];
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
     return kt;
   };
   // Key tile kt -> stage: K rows (rows at or past klim fetch row klim-1, masked later) and
-  // the V^T columns k0 .. k0+63 (zero past klim in the workspace).
+  // the V^T columns k0 .. k0+127 (zero past klim in the workspace, whose rows are padded
+  // to a multiple of 128).
   // Both copies go through buffer resources based at the tile (see buf_rsrc). The V^T
   // tile spans D rows of the transposed workspace: its offsets, below D * Np <= N * d +
   // 63 d, stay under 2^32 because the C ABI keeps N * d below 2^31 (offsets and sizes are
@@ -166,8 +168,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
       const int krow = byte / D;
       const int kch = ((byte % D) >> 4) ^ swz_k8<D>(krow);
       buf2lds16(rk, (min(k0 + krow, klim - 1) - k0) * D + kch * 16, dK + g * 1024);
-      const int vrow = byte >> 6;
-      const int vch = ((byte & 63) >> 4) ^ swz_v8(vrow);
+      const int vrow = byte >> 7;
+      const int vch = ((byte & 127) >> 4) ^ swz_v8(vrow);
       buf2lds16(rv, (int)((uint32_t)vrow * (uint32_t)p.Np + vch * 16), dV + g * 1024);
     }
   };
@@ -201,13 +203,16 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 
   // LDS operand offsets. K: lane row r reads key pi(r), chunks 4*st + 2*hi + e (e = 0, 1);
   // the step is bit 2 of the chunk, i.e. XOR (st << 6) on the byte offset. V^T: lane row r
-  // of column block j reads d-row 32j + r, chunks hi and 2 + hi.
+  // of column block j reads d-row 32j + r, chunks 4*kh + hi and 4*kh + 2 + hi for the
+  // tile's 64-key half kh.
   const int krow0 = pi_row(l32);
-  int k_off[2], v_off[2];
+  int k_off[2], v_off[2][2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     k_off[e] = krow0 * D + 16 * ((2 * hi + e) ^ swz_k8<D>(krow0));
-    v_off[e] = l32 * 64 + 16 * ((2 * e + hi) ^ swz_v8(l32));
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+      v_off[kh][e] = l32 * 128 + 16 * ((4 * kh + 2 * e + hi) ^ swz_v8(l32));
   }
 
   auto compute = [&](int kt, const char* sK, const char* sV) {
@@ -215,9 +220,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
     if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;
     if (bmw && !bm_keep(bmw, k0 >> 7)) return;
 
-    f32x16 s[2];
+    f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
     // Element i of lane half hi in block kb is key k0 + 32*kb + 16*hi + i.
     if (k0 + BC - 1 > qw + rl || k0 < qw + 31 - ll || k0 + BC > klim) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + 16 * hi + i;
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
     // max on the previous one's result).
     float mq[4] = {-kInf, -kInf, -kInf, -kInf};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mq[i & 3] = fmaxf(mq[i & 3], s[kb][i]);
     float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = fast_exp2(s[kb][i] * p.sc - m_use);
@@ -279,27 +284,31 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
       }
     l_run += lsum;  // the normaliser uses the unrounded probabilities
 
-    // P^T as the B operand: byte 16*kb + i = E4M3 of s[kb][i] (nearest even).
-    i32x8 pf;
+    // P^T as the B operand of 64-key half kh: byte 16*(kb - 2*kh) + i = E4M3 of s[kb][i]
+    // (nearest even).
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, i0 = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0 + 2], s[kb][i0 + 3], x, true);
-      pf[w] = x;
-    }
+    for (int kh = 0; kh < 2; ++kh) {
+      i32x8 pf;
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const char* base = sV + j * 32 * 64;
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(base + v_off[0]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(base + v_off[1]);
-      i32x8 a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = (int)a0[e];
-        a[4 + e] = (int)a1[e];
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * kh + (w >> 2), i0 = 4 * (w & 3);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0 + 2], s[kb][i0 + 3], x, true);
+        pf[w] = x;
       }
-      acc[j] = mfma_f8(a, pf, acc[j]);
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        const char* base = sV + j * 32 * 128;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(base + v_off[kh][0]);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(base + v_off[kh][1]);
+        i32x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = (int)a0[e];
+          a[4 + e] = (int)a1[e];
+        }
+        acc[j] = mfma_f8(a, pf, acc[j]);
+      }
     }
   };
 

@@ -195,7 +195,8 @@ int fa_bwd_dropout(int dtype, const void* q, const void* k, const void* v, const
  *     [B][H][N], the natural-log logsumexp of the scores (-inf for a row with no allowed
  *     key, whose o is 0).
  *   workspace: DEVICE, 256-byte aligned, fa_fwd_fp8_workspace_bytes(B, H, N, d) bytes:
- *     receives v transposed to [B][H][d][N rounded up to 64] (zero past N).
+ *     receives v transposed to [B][H][d][N rounded up to 128] (zero past N and past the
+ *     batch entry's kv_len).
  *   d must be 64 or 128; scale finite and nonzero; each descale finite and > 0.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED_D, FA_ERR_SCALE, FA_ERR_ALIGN
  * (q, k, v, o 16 bytes, lse and kv_len 4, workspace 256), FA_ERR_ALIAS (o, lse, workspace
