@@ -506,15 +506,19 @@ def main():
     pad = "false" if wl.d == kd else "true"                    # rows narrower than kd
     dc = wl.d if wl.d in (32, 96) else kd                      # head dim computed on
     nw = 4 if kd == 256 else 8                                 # waves per workgroup
-    # the 64-wide forward and dQ kernels run four-wave workgroups under a block table
+    # the 64-wide forward and dQ kernels run four-wave workgroups under a block table; the
+    # forward also when its eight-wave grid is under two workgroups per CU
     nwq = 4 if kd == 64 and wl.mask == "block" and dr == "false" else nw
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    small = math.ceil(wl.N / 256) * wl.B * wl.H < 2 * cus
+    nwf = 4 if kd == 64 and dr == "false" and (wl.mask == "block" or small) else nw
     rk = kd == 128 or (kd == 64 and dr == "false")             # one-wave dK/dV kernel
     k_dkdv = (f"bwd_dkdv_rk_kernel<{tn}, {kd}, {dr}, {pad}, {dc}>" if rk
               else f"bwd_dkdv_kernel<{tn}, {kd}, {dr}, {pad}, {dc}, {nw}>")
     bc = 128 if kd == 128 else 64                              # forward key tile
     bcq = 128 if kd <= 128 else 64                             # dQ key tile
     k_dq = f"bwd_dq_kernel<{tn}, {kd}, {bcq}, {dr}, {pad}, {dc}, {nwq}>"
-    k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwq}>"
+    k_fwd = f"fwd_kernel<{tn}, {kd}, {bc}, {dr}, {pad}, {dc}, {nwf}>"
     rec = {
         "metric": METRIC, "value": round(tf_step, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -26,6 +26,8 @@
 //   the register layout of the B operand of O^T += V^T P^T (no LDS round trip for P);
 //   the V^T operand is read from the row-major tile with LDS transpose loads.
 //   Q stays in registers for the whole workgroup; O^T accumulates in registers.
+#include <atomic>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -318,6 +320,24 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 4 : 1))) void fwd_kernel
   }
 }
 
+// Compute units of the current device, looked up once per device (concurrent first calls
+// may both look it up; they store the same value).
+unsigned device_cus() {
+  static std::atomic<unsigned> cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  unsigned n = cus[dev].load(std::memory_order_relaxed);
+  if (!n) {
+    int a = 0;
+    if (hipDeviceGetAttribute(&a, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        a <= 0)
+      a = 256;
+    n = (unsigned)a;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
 template <typename T, bool DROP>
@@ -344,11 +364,13 @@ hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
   else if (d > 64)
     hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
-  else if (!DROP && p.blockmask) {
+  else if (!DROP && (p.blockmask || grid.x < 2 * device_cus())) {
     // 64-wide layout with a block table: four-wave workgroups of 128 queries, one row of
     // the table each. The two query blocks of an eight-wave workgroup copy the union of
     // the key blocks either keeps, and each wave idles through the tiles that only the
-    // other block keeps. Four waves per SIMD, as with eight-wave workgroups.
+    // other block keeps. Four waves per SIMD, as with eight-wave workgroups. The same
+    // kernel serves grids too small to give every CU its two eight-wave workgroups: twice
+    // as many workgroups of half the work fill the CUs more evenly.
     const dim3 grid4((unsigned)((p.N + 127) / 128) * bh);
     if (d == 64)
       hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, false, 64, 4>), grid4, dim3(256), 0, stream, p);
