@@ -494,7 +494,9 @@ def main():
     ms_fwd = time_loop(torch, f_fwd, args.steps, args.warmup)
     ms_bwd = time_loop(torch, f_bwd, args.steps, args.warmup)
     ms_pre = time_loop(torch, f_pre, args.steps, args.warmup)
-    ms_bwd_main = max(ms_bwd - ms_pre, 1e-6)
+    # The backward's row statistics (D, LSE * log2(e)) are formed at the start of its dQ
+    # kernel; the standalone preprocess entry point is timed apart and not subtracted.
+    ms_bwd_main = ms_bwd
 
     tf_step = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
     tf_fwd = fl_fwd / (ms_fwd * 1e-3) / 1e12
@@ -539,7 +541,7 @@ def main():
                       "bwd": timing_record(ms_bwd), "bwd_preprocess": timing_record(ms_pre)},
         "fwd_bwd_tflops_at_median": round((fl_fwd + fl_bwd) / (ms_step.median * 1e-3) / 1e12, 2),
         "fwd_tflops_at_median": round(fl_fwd / (ms_fwd.median * 1e-3) / 1e12, 2),
-        "roofline": {"kernel": f"{k_dkdv} + {k_dq} (backward minus its preprocess)",
+        "roofline": {"kernel": f"{k_dq} (row statistics at its start) + {k_dkdv} (the whole backward)",
                      "bound": "mfma", "achieved": round(tf_bwd_main, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf_bwd_main / MFMA_BF16_PEAK_TFLOPS, 4),

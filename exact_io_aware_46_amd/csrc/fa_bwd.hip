@@ -855,21 +855,37 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   int kt = next_tile(kt_lo);
   if (kt < nkt) issue(kt, sK0, sV0);
 
-  // This lane's query row of Q and dO, as B operands of S^T = K Q^T and dP^T = V dO^T;
-  // its log2-scaled LSE and D.
+  // This lane's query row of Q and dO, as B operands of S^T = K Q^T and dP^T = V dO^T
+  // (lane half hi holds columns 16s + 8hi .. +7 of step s). The row statistics of the
+  // backward are formed here (step B0): D = rowsum(dO * O) from the same halves of the
+  // O row, and LSE * log2(e), +inf for a row with no allowed key (so that P = 0). This
+  // kernel runs first; it stores both into the workspace for the dK/dV pass.
   typename T::vec8 qf[NS], gf[NS];
+  float dpart = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
     if (myq < N && (!PAD || 2 * s + hi < cha)) {
       x = ldg16(Q + (size_t)myq * ld + 16 * s + 8 * hi);
       y = ldg16(dO + (size_t)myq * ld + 16 * s + 8 * hi);
+      z = ldg16(p.o + hoff + (size_t)myq * ld + 16 * s + 8 * hi);
     }
     qf[s] = as_vec<T>(x);
     gf[s] = as_vec<T>(y);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dpart += T::lo(z[w]) * T::lo(y[w]);
+      dpart += T::hi(z[w]) * T::hi(y[w]);
+    }
   }
-  const float lq = myq < N ? p.lse2[(size_t)bh * N + myq] : kInf;  // +inf: P = 0
-  const float ndq = myq < N ? p.ndelta[(size_t)bh * N + myq] : 0.f;  // -D
+  const float dq_row = xhalf_sum(dpart);
+  const float lse_row = myq < N ? p.lse[(size_t)bh * N + myq] : -kInf;
+  const float lq = lse_row == -kInf ? kInf : lse_row * kLog2e;  // +inf: P = 0
+  const float ndq = myq < N ? -dq_row : 0.f;                     // -D
+  if (myq < N && hi == 0) {
+    p.ndelta[(size_t)bh * N + myq] = ndq;
+    p.lse2[(size_t)bh * N + myq] = lq;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -1027,6 +1043,28 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
 
 template <typename T, int D, bool DROP, bool PAD, int DC, int NW = 8>
 hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
+  // The dQ pass runs first: it forms the row statistics (D, LSE * log2(e)) that the dK/dV
+  // pass reads from the workspace.
+  // It keeps one 32-key block of S and dP live at a time, so its key tiles can hold 128
+  // keys (one barrier and copy round per 128 keys; 128 KB of LDS on the 128 layout, 64 KB
+  // on the 64 one) at no register cost; the 256 layout's LDS holds 64.
+  constexpr int BCQ = D <= 128 ? 128 : 64;
+  bool dq_done = false;
+  if constexpr (D == 64 && !DROP) {
+    // With a block table, four-wave workgroups of 128 queries (one table row each), as in
+    // the forward: no wave idles through key tiles that only another query block keeps.
+    if (p.blockmask) {
+      const dim3 g_q4((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, 4>), g_q4, dim3(256), 0,
+                         stream, p);
+      dq_done = true;
+    }
+  }
+  if (!dq_done)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
+                       stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // 128-wide layout (head dims 65 .. 128): one wave per SIMD with K and V in registers,
   // 1.5% faster than the two-wave kernel at d = 128. d = 96 runs it too, although 0.8%
   // slower there, so that every head dim of the layout sums in the order of d = 128 (its
@@ -1039,32 +1077,11 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC, NW>), g_kv, dim3(64 * NW), 0,
                        stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // The dQ pass keeps one 32-key block of S and dP live at a time, so its key tiles can
-  // hold 128 keys (one barrier and copy round per 128 keys; 128 KB of LDS on the 128
-  // layout, 64 KB on the 64 one) at no register cost; the 256 layout's LDS holds 64.
-  constexpr int BCQ = D <= 128 ? 128 : 64;
-  if constexpr (D == 64 && !DROP) {
-    // With a block table, four-wave workgroups of 128 queries (one table row each), as in
-    // the forward: no wave idles through key tiles that only another query block keeps.
-    if (p.blockmask) {
-      const dim3 g_q4((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, 4>), g_q4, dim3(256), 0,
-                         stream, p);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
-                     stream, p);
   return hipGetLastError();
 }
 
 template <typename T, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
-  const int rows = p.B * p.H * p.N;
-  hipError_t e = launch_pre_t<T>(p.o, p.dO, p.lse, p.ndelta, p.lse2, rows, d, -1.f, stream);
-  if (e != hipSuccess) return e;
   const unsigned bh = (unsigned)(p.B * p.H);
   const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh);
   if (d > 128) {  // 256-wide tiles, four waves: dK/dV 64 keys, dQ 128 queries per workgroup

@@ -106,7 +106,8 @@ int fa_fwd_window(const fa_bf16* q, const fa_bf16* k, const fa_bf16* v, fa_bf16*
 
 /* Backward preprocess: delta[b][h][i] = sum_c dO[b][h][i][c] * O[b][h][i][c], summed in
  * fp32 over the given bf16 O and dO. This is the row statistic D of the softmax gradient
- * dS = P * (dP - D). fa_bwd runs it itself; it is exported for callers that want D. */
+ * dS = P * (dP - D). fa_bwd forms D itself, at the start of its dQ pass; this entry point
+ * is exported for callers that want D on its own. */
 int fa_bwd_preprocess(const fa_bf16* o, const fa_bf16* dO, float* delta, int B, int H, int N,
                       int d, void* stream);
 
