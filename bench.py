@@ -247,6 +247,7 @@ def fp8_main(args, torch, wl, x):
                       "items": PAGE_CONTEXT}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = fp8_cpu_baseline(x)
+        rec["cpu_baseline"]["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
     print(json.dumps(rec), flush=True)
 
 
@@ -570,6 +571,7 @@ def main():
         rec["footprint"] = footprint_sweep(torch, wl)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x)
+        rec["cpu_baseline"]["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
     print(json.dumps(rec), flush=True)
 
 
