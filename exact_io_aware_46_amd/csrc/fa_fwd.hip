@@ -180,7 +180,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 4 : 1))) void fwd_kernel
   auto compute = [&](int kt, const char* sK, const char* sV) {
     const int k0 = kt * BC;
     if (qw >= N || k0 > qw + 31 + rl || k0 + BC - 1 < qw - ll) return;  // nothing allowed
-    if (bmw && !bm_keep(bmw, k0 >> 7)) return;                   // block masked for this wave
+    if (bmw && !bm_keep(bmw, k0 >> 7)) return;  // block masked for this wave
 
     f32x16 s[KB];
 #pragma unroll
