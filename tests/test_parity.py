@@ -141,6 +141,22 @@ def test_all_ones_block_mask_is_bitwise_dense(d):
         assert _bits_equal(getattr(a, name), getattr(b, name)), name
 
 
+@pytest.mark.parametrize("d", [64, 40])
+def test_four_and_eight_wave_kernels_are_bitwise_equal(d):
+    """On the 64-wide layout the forward and dQ kernels run four-wave workgroups under a
+    block table (and the forward also for small grids), eight-wave ones otherwise. Each
+    wave computes its rows the same way in both, so on a grid large enough for the
+    eight-wave kernels (128 heads x 1024 queries: 512 workgroups) an all-ones table must
+    give every output bit for bit as no table."""
+    N, H = 1024, 128
+    q, k, v, do = inp.custom_inputs(1, H, N, d, seed=241 + d)
+    say(f"[bitexact] four- vs eight-wave kernels d={d}")
+    a = Run(q, k, v, do, 0.125, True)
+    b = Run(q, k, v, do, 0.125, True, blockmask=np.ones((8, 8), np.uint8))
+    for name in ("o", "lse", "dq_", "dk_", "dv_"):
+        assert _bits_equal(getattr(a, name), getattr(b, name)), name
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_block_table_at_odd_addresses_is_bitwise_the_aligned_one(d):
     """The kernels read the block table through the scalar unit, a dword at a time, and
