@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -92,6 +93,8 @@ def parse():
     ap.add_argument("--workload", default="long_causal_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-footprint", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="with the default workload, skip timing the four other workloads")
     ap.add_argument("--no-device-sample", action="store_true",
                     help="skip the amd-smi clock/power sample (profiling runs)")
     ap.add_argument("--eager", action="store_true",
@@ -419,7 +422,6 @@ def measured_traffic(workload, kind, kernels):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
     (profiles/traffic_<workload>.md, copy-calibrated), or None when there is no summary
     or the kernel's sources have changed since the counters were taken."""
-    import re
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -434,6 +436,66 @@ def measured_traffic(workload, kind, kernels):
                        for k in kernels))
     except KeyError:
         return None
+
+
+OTHER_CONFIGS = ("single_head_256", "gpt2s_causal_1k", "bertl_kpad_512", "blocksparse_8k")
+
+
+def other_configs(torch, inp, steps, warmup):
+    """The other four workloads the headline metric is stated beside (one head of 256,
+    GPT-2-small causal 1K, BERT-large with key padding, block-sparse 8K), timed like the
+    main one with direct calls. Per workload: fwd, bwd and fwd+bwd times and TFLOP/s, and
+    the HBM rate of the forward and backward: the compulsory bytes (forward 8Nd + 4N and
+    backward 18Nd + 16N per head, bf16), and the copy-calibrated bytes that rocprofv3
+    measured for these kernels when that summary is present and current, over the time."""
+    out = {}
+    for name in OTHER_CONFIGS:
+        wl = inp.WORKLOADS[name]
+        x = inp.make_inputs(wl)
+        pairs = workload_pairs(x)
+        fl_fwd, fl_bwd = 4.0 * pairs * wl.d, 10.0 * pairs * wl.d
+        buf = Buffers(x, torch)
+        t_fwd = time_loop(torch, buf.fwd, steps, warmup)
+        t_bwd = time_loop(torch, buf.bwd, steps, warmup)
+        t_step = time_loop(torch, buf.step, steps, warmup)
+        heads = wl.B * wl.H
+        comp_fwd = heads * (8 * wl.N * wl.d + 4 * wl.N)
+        comp_bwd = heads * (18 * wl.N * wl.d + 16 * wl.N)
+        rec = {"fwd_ms": round(float(t_fwd), 4), "bwd_ms": round(float(t_bwd), 4),
+               "step_ms": round(float(t_step), 4),
+               "fwd_median_ms": round(t_fwd.median, 4), "step_median_ms": round(t_step.median, 4),
+               "fwd_tflops": round(fl_fwd / (t_fwd * 1e-3) / 1e12, 2),
+               "bwd_tflops": round(fl_bwd / (t_bwd * 1e-3) / 1e12, 2),
+               "fwd_bwd_tflops": round((fl_fwd + fl_bwd) / (t_step * 1e-3) / 1e12, 2),
+               "fwd_bwd_frac_of_peak": round((fl_fwd + fl_bwd) / (t_step * 1e-3) / 1e12
+                                             / MFMA_BF16_PEAK_TFLOPS, 4),
+               "fwd_compulsory_gbs": round(comp_fwd / (t_fwd * 1e-3) / 1e9, 1),
+               "bwd_compulsory_gbs": round(comp_bwd / (t_bwd * 1e-3) / 1e9, 1)}
+        m = re.search(r"<!-- traffic-json: (.*) -->", _read(os.path.join(
+            ROOT, "profiles", f"traffic_{name}.md")))
+        if m:
+            blob = json.loads(m.group(1))
+            cur = all(blob.get("source_sha256", {}).get(k) == source_hash(k)
+                      for k in ("fwd_kernel", "bwd_kernel"))
+            if cur:
+                kern = blob["kernels"]
+                fw = sum(v["read_bytes"] + v["write_bytes"] for k, v in kern.items()
+                         if k.startswith("fwd_kernel"))
+                bw = sum(v["read_bytes"] + v["write_bytes"] for k, v in kern.items()
+                         if k.startswith("bwd_dkdv") or k.startswith("bwd_dq"))
+                rec["fwd_measured_gbs"] = round(fw / (t_fwd * 1e-3) / 1e9, 1)
+                rec["bwd_measured_gbs"] = round(bw / (t_bwd * 1e-3) / 1e9, 1)
+        out[name] = rec
+        del buf, x
+    return out
+
+
+def _read(path):
+    try:
+        with open(path) as fh:
+            return fh.read()
+    except OSError:
+        return ""
 
 
 def cpu_baseline(x, heads=4):
@@ -569,6 +631,8 @@ def main():
     if not args.no_footprint and wl.name == "long_causal_16k":
         del buf
         rec["footprint"] = footprint_sweep(torch, wl)
+    if not args.no_other_configs and wl.name == "long_causal_16k":
+        rec["other_configs"] = other_configs(torch, inp, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x)
         rec["cpu_baseline"]["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
