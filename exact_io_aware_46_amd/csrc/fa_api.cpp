@@ -107,7 +107,7 @@ int fwd_impl(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v,
   for (const void* in : {(const void*)q, (const void*)k, (const void*)v})
     if (overlap(ro, span(in, tbytes)) || overlap(rl, span(in, tbytes))) return FA_ERR_ALIAS;
 
-  fa::FwdParams p;
+  fa::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.blockmask = blockmask;
   p.kv_len = kv_len;
@@ -246,7 +246,7 @@ int bwd_entry(int dtype, const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (overlap(rw, r)) return FA_ERR_ALIAS;
 
   char* ws = static_cast<char*>(workspace);
-  BwdParams p;
+  BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.dO = dO;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.blockmask = blockmask;
@@ -375,7 +375,7 @@ int fa_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, fa_bf16* o,
     if (overlap(ro, ri) || overlap(rl, ri) || overlap(rw, ri)) return FA_ERR_ALIAS;
   }
 
-  fa::Fp8Params p;
+  fa::Fp8Params p{};
   p.q = q; p.k = k; p.vt = static_cast<const uint8_t*>(workspace);
   p.o = o; p.lse = lse;
   p.blockmask = blockmask;

@@ -117,9 +117,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float sD1[64];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BH = p.nbh;  // heads of this launch, from p.bh0 on
   const int kt = (int)(blockIdx.x / BH);  // key tiles with most work (causal) go first
-  const int bh = (int)(blockIdx.x % BH);
+  const int bh = p.bh0 + (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -470,9 +470,9 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_rk_kernel(Bw
   __shared__ __attribute__((aligned(256))) float sD1[64];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BH = p.nbh;  // heads of this launch, from p.bh0 on
   const int kt = (int)(blockIdx.x / BH);  // key tiles with most work (causal) go first
-  const int bh = (int)(blockIdx.x % BH);
+  const int bh = p.bh0 + (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -772,10 +772,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sV1[TILE];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BH = p.nbh;  // heads of this launch, from p.bh0 on
   const int nqt = (N + BR - 1) / BR;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest (causal) tiles first
-  const int bh = (int)(blockIdx.x % BH);
+  const int bh = p.bh0 + (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave: readfirstlane tells the compiler so, which
@@ -1021,17 +1021,28 @@ hipError_t launch_pre_t(const uint16_t* o, const uint16_t* dO, const float* lse,
                         float* lse2, int rows, int d, float dsign, hipStream_t stream) {
   const int dt = d > 128 ? 256 : d > 64 ? 128 : 64;  // threads per row cover dt columns
   const int rpb = 256 / (dt / 8);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  if (dt == 256)
-    hipLaunchKernelGGL((bwd_pre_kernel<T, 256>), grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows, d, dsign);
-  else if (dt == 128)
-    hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows, d, dsign);
-  else
-    hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), grid, dim3(256), 0, stream, o, dO, lse, delta,
-                       lse2, rows, d, dsign);
-  return hipGetLastError();
+  // At most 2^24 - 1 workgroups of 256 per launch (a dispatch counts work-items in 32
+  // bits); more rows go out as several launches over consecutive rows.
+  const long long per = (long long)(0xFFFFFFFFu / 256) * rpb;
+  for (long long r0 = 0; r0 < rows; r0 += per) {
+    const int n = (int)std::min<long long>(per, rows - r0);
+    const size_t e0 = (size_t)r0 * d;
+    const float* l = lse ? lse + r0 : nullptr;
+    float* l2 = lse2 ? lse2 + r0 : nullptr;
+    const dim3 grid((unsigned)((n + rpb - 1) / rpb));
+    if (dt == 256)
+      hipLaunchKernelGGL((bwd_pre_kernel<T, 256>), grid, dim3(256), 0, stream, o + e0,
+                         dO + e0, l, delta + r0, l2, n, d, dsign);
+    else if (dt == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), grid, dim3(256), 0, stream, o + e0,
+                         dO + e0, l, delta + r0, l2, n, d, dsign);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), grid, dim3(256), 0, stream, o + e0,
+                         dO + e0, l, delta + r0, l2, n, d, dsign);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const float* lse,
@@ -1042,28 +1053,35 @@ hipError_t launch_bwd_preprocess(const uint16_t* o, const uint16_t* dO, const fl
 }
 
 template <typename T, int D, bool DROP, bool PAD, int DC, int NW = 8>
-hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stream) {
+hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
+  // Each pass runs over (tile, head) workgroups, in one launch unless the grid holds more
+  // work-items than a dispatch can count.
+  const long long nq = D > 128 ? (p.N + 127) / 128 : (p.N + 255) / 256;  // NW query rows each
+  const long long nk = D > 128 ? (p.N + 63) / 64 : (p.N + 127) / 128;
   // The dQ pass runs first: it forms the row statistics (D, LSE * log2(e)) that the dK/dV
   // pass reads from the workspace.
   // It keeps one 32-key block of S and dP live at a time, so its key tiles can hold 128
   // keys (one barrier and copy round per 128 keys; 128 KB of LDS on the 128 layout, 64 KB
   // on the 64 one) at no register cost; the 256 layout's LDS holds 64.
   constexpr int BCQ = D <= 128 ? 128 : 64;
+  hipError_t e = hipSuccess;
   bool dq_done = false;
   if constexpr (D == 64 && !DROP) {
     // With a block table, four-wave workgroups of 128 queries (one table row each), as in
     // the forward: no wave idles through key tiles that only another query block keeps.
     if (p.blockmask) {
-      const dim3 g_q4((unsigned)((p.N + 127) / 128) * (unsigned)(p.B * p.H));
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, 4>), g_q4, dim3(256), 0,
-                         stream, p);
+      e = launch_by_heads(p, (p.N + 127) / 128, 256, [&](dim3 g, const BwdParams& q) {
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, 4>), g, dim3(256), 0,
+                           stream, q);
+      });
       dq_done = true;
     }
   }
   if (!dq_done)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g_q, dim3(64 * NW), 0,
-                       stream, p);
-  const hipError_t e = hipGetLastError();
+    e = launch_by_heads(p, nq, 64 * NW, [&](dim3 g, const BwdParams& q) {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, BCQ, DROP, PAD, DC, NW>), g, dim3(64 * NW), 0,
+                         stream, q);
+    });
   if (e != hipSuccess) return e;
   // 128-wide layout (head dims 65 .. 128): one wave per SIMD with K and V in registers,
   // 1.5% faster than the two-wave kernel at d = 128. d = 96 runs it too, although 0.8%
@@ -1073,31 +1091,31 @@ hipError_t launch_main(const BwdParams& p, dim3 g_kv, dim3 g_q, hipStream_t stre
   // cover each other's waits: 2-11% faster than the two-wave kernel there. With dropout
   // it would spill at that budget, and the two-wave kernel stays.
   if constexpr (NW == 8 && (D == 128 || (D == 64 && !DROP)))
-    hipLaunchKernelGGL((bwd_dkdv_rk_kernel<T, D, DROP, PAD, DC>), g_kv, dim3(256), 0, stream, p);
+    return launch_by_heads(p, nk, 256, [&](dim3 g, const BwdParams& q) {
+      hipLaunchKernelGGL((bwd_dkdv_rk_kernel<T, D, DROP, PAD, DC>), g, dim3(256), 0, stream,
+                         q);
+    });
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC, NW>), g_kv, dim3(64 * NW), 0,
-                       stream, p);
-  return hipGetLastError();
+    return launch_by_heads(p, nk, 64 * NW, [&](dim3 g, const BwdParams& q) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, DROP, PAD, DC, NW>), g, dim3(64 * NW), 0,
+                         stream, q);
+    });
 }
 
 template <typename T, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, int d, hipStream_t stream) {
-  const unsigned bh = (unsigned)(p.B * p.H);
-  const dim3 g_kv((unsigned)((p.N + 127) / 128) * bh);
   if (d > 128) {  // 256-wide tiles, four waves: dK/dV 64 keys, dQ 128 queries per workgroup
-    const dim3 g_kv4((unsigned)((p.N + 63) / 64) * bh), g_q4((unsigned)((p.N + 127) / 128) * bh);
-    if (d == 256) return launch_main<T, 256, DROP, false, 256, 4>(p, g_kv4, g_q4, stream);
-    return launch_main<T, 256, DROP, true, 256, 4>(p, g_kv4, g_q4, stream);
+    if (d == 256) return launch_main<T, 256, DROP, false, 256, 4>(p, stream);
+    return launch_main<T, 256, DROP, true, 256, 4>(p, stream);
   }
-  const dim3 g_q((unsigned)((p.N + 255) / 256) * bh);
   // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
   // head dims run the next kernel up on zero-padded tiles.
-  if (d == 128) return launch_main<T, 128, DROP, false, 128>(p, g_kv, g_q, stream);
-  if (d == 96) return launch_main<T, 128, DROP, true, 96>(p, g_kv, g_q, stream);
-  if (d > 64) return launch_main<T, 128, DROP, true, 128>(p, g_kv, g_q, stream);
-  if (d == 64) return launch_main<T, 64, DROP, false, 64>(p, g_kv, g_q, stream);
-  if (d == 32) return launch_main<T, 64, DROP, true, 32>(p, g_kv, g_q, stream);
-  return launch_main<T, 64, DROP, true, 64>(p, g_kv, g_q, stream);
+  if (d == 128) return launch_main<T, 128, DROP, false, 128>(p, stream);
+  if (d == 96) return launch_main<T, 128, DROP, true, 96>(p, stream);
+  if (d > 64) return launch_main<T, 128, DROP, true, 128>(p, stream);
+  if (d == 64) return launch_main<T, 64, DROP, false, 64>(p, stream);
+  if (d == 32) return launch_main<T, 64, DROP, true, 32>(p, stream);
+  return launch_main<T, 64, DROP, true, 64>(p, stream);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, hipStream_t stream) {

@@ -62,12 +62,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 4 : 1))) void fwd_kernel
   __shared__ __attribute__((aligned(1024))) char sV1[TILE];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BH = p.nbh;  // heads of this launch, from p.bh0 on
   const int nqt = (N + BR - 1) / BR;
   // Heaviest query tiles (largest index under a causal mask) are dispatched first; the
   // (b, h) index varies fastest so that consecutive workgroups share K and V.
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  const int bh = p.bh0 + (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   // Read as uniform: per-wave tests become scalar branches and wave-derived values live in
@@ -342,49 +342,39 @@ unsigned device_cus() {
 
 template <typename T, bool DROP>
 hipError_t launch_fwd_t(const FwdParams& p, int d, hipStream_t stream) {
-  const unsigned bh = (unsigned)(p.B * p.H);
+  // Each kernel runs over (query tile, head) workgroups, in one launch unless the grid
+  // holds more work-items than a dispatch can count.
+#define FA_FWD(BR, NT, ...)                                                                \
+  return launch_by_heads(p, (p.N + (BR) - 1) / (BR), NT, [&](dim3 g, const FwdParams& q) { \
+    hipLaunchKernelGGL((fwd_kernel<T, __VA_ARGS__>), g, dim3(NT), 0, stream, q);           \
+  })
   if (d > 128) {  // 256-wide tiles, four waves of 32 queries
-    const dim3 grid((unsigned)((p.N + 127) / 128) * bh);
-    if (d == 256)
-      hipLaunchKernelGGL((fwd_kernel<T, 256, 64, DROP, false, 256, 4>), grid, dim3(256), 0,
-                         stream, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, 256, 64, DROP, true, 256, 4>), grid, dim3(256), 0,
-                         stream, p);
-    return hipGetLastError();
+    if (d == 256) FA_FWD(128, 256, 256, 64, DROP, false, 256, 4);
+    FA_FWD(128, 256, 256, 64, DROP, true, 256, 4);
   }
-  const dim3 grid((unsigned)((p.N + 255) / 256) * bh);
+  const long long tiles8 = ((long long)p.N + 255) / 256 * p.B * p.H;
   // d = 64 and 128 run their own kernels, 32 and 96 compute on the 64 / 128 layout, other
   // head dims run the next kernel up on zero-padded tiles. The 128 layout takes key tiles
   // of 128 (one barrier, one copy round and one row-maximum reduction per 128 keys); the
   // 64 layout's registers and the 256 layout's LDS hold tiles of 64.
-  if (d == 128)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, false, 128, 8>), grid, dim3(512), 0, stream, p);
-  else if (d == 96)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 96, 8>), grid, dim3(512), 0, stream, p);
-  else if (d > 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 128, 128, DROP, true, 128, 8>), grid, dim3(512), 0, stream, p);
-  else if (!DROP && (p.blockmask || grid.x < 2 * device_cus())) {
+  if (d == 128) FA_FWD(256, 512, 128, 128, DROP, false, 128, 8);
+  if (d == 96) FA_FWD(256, 512, 128, 128, DROP, true, 96, 8);
+  if (d > 64) FA_FWD(256, 512, 128, 128, DROP, true, 128, 8);
+  if (!DROP && (p.blockmask || tiles8 < 2LL * device_cus())) {
     // 64-wide layout with a block table: four-wave workgroups of 128 queries, one row of
     // the table each. The two query blocks of an eight-wave workgroup copy the union of
     // the key blocks either keeps, and each wave idles through the tiles that only the
     // other block keeps. Four waves per SIMD, as with eight-wave workgroups. The same
     // kernel serves grids too small to give every CU its two eight-wave workgroups: twice
     // as many workgroups of half the work fill the CUs more evenly.
-    const dim3 grid4((unsigned)((p.N + 127) / 128) * bh);
-    if (d == 64)
-      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, false, 64, 4>), grid4, dim3(256), 0, stream, p);
-    else if (d == 32)
-      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, true, 32, 4>), grid4, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, 64, 64, false, true, 64, 4>), grid4, dim3(256), 0, stream, p);
-  } else if (d == 64)
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, false, 64, 8>), grid, dim3(512), 0, stream, p);
-  else if (d == 32)
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 32, 8>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, 64, 64, DROP, true, 64, 8>), grid, dim3(512), 0, stream, p);
-  return hipGetLastError();
+    if (d == 64) FA_FWD(128, 256, 64, 64, false, false, 64, 4);
+    if (d == 32) FA_FWD(128, 256, 64, 64, false, true, 32, 4);
+    FA_FWD(128, 256, 64, 64, false, true, 64, 4);
+  }
+  if (d == 64) FA_FWD(256, 512, 64, 64, DROP, false, 64, 8);
+  if (d == 32) FA_FWD(256, 512, 64, 64, DROP, true, 32, 8);
+  FA_FWD(256, 512, 64, 64, DROP, true, 64, 8);
+#undef FA_FWD
 }
 
 hipError_t launch_fwd(const FwdParams& p, int d, int dtype, hipStream_t stream) {

@@ -74,10 +74,11 @@ __device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
 template <int D>
 __global__ __launch_bounds__(256) void vt_fp8_kernel(const uint8_t* __restrict__ v,
                                                      uint8_t* __restrict__ vt, int N, int Np,
-                                                     int H, const int32_t* __restrict__ kv_len) {
+                                                     int H, const int32_t* __restrict__ kv_len,
+                                                     int bh0) {
   constexpr int LW = D / 4 + 1;  // words per padded LDS row
   __shared__ uint32_t tile[64 * LW];
-  const int bh = (int)blockIdx.y, k0 = (int)blockIdx.x * 64, tid = (int)threadIdx.x;
+  const int bh = bh0 + (int)blockIdx.y, k0 = (int)blockIdx.x * 64, tid = (int)threadIdx.x;
   const int klim = kv_len ? min(N, max(kv_len[bh / H], 0)) : N;
   const uint8_t* src = v + (size_t)bh * N * D;
   for (int e = tid; e < 64 * (D / 4); e += 256) {
@@ -116,10 +117,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
   __shared__ __attribute__((aligned(1024))) char sV1[VT];
 
   const int N = p.N;
-  const int BH = p.B * p.H;
+  const int BH = p.nbh;  // heads of this launch, from p.bh0 on
   const int nqt = (N + BR - 1) / BR;
   const int qt = nqt - 1 - (int)(blockIdx.x / BH);  // heaviest (causal) tiles first
-  const int bh = (int)(blockIdx.x % BH);
+  const int bh = p.bh0 + (int)(blockIdx.x % BH);
   const int b = bh / p.H;
   const int tid = threadIdx.x;
   // Read as uniform (scalar per-wave tests, wave-derived values in SGPRs): 2.3% faster.
@@ -350,22 +351,26 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 
 hipError_t launch_fwd_fp8(const Fp8Params& p, const uint8_t* v, uint8_t* vt, int d,
                           hipStream_t stream) {
-  const unsigned bh = (unsigned)(p.B * p.H);
-  const dim3 tgrid((unsigned)(p.Np / 64), bh);
-  if (d == 128)
-    hipLaunchKernelGGL((vt_fp8_kernel<128>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
-                       p.H, p.kv_len);
-  else
-    hipLaunchKernelGGL((vt_fp8_kernel<64>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
-                       p.H, p.kv_len);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((p.N + 255) / 256) * bh);
-  if (d == 128)
-    hipLaunchKernelGGL((fwd_fp8_kernel<128>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_fp8_kernel<64>), grid, dim3(512), 0, stream, p);
-  return hipGetLastError();
+  // The transpose takes (64-key block, head) workgroups, the heads along y, at most 65535
+  // of them per launch.
+  const long long bh = (long long)p.B * p.H;
+  for (long long h0 = 0; h0 < bh; h0 += 65535) {
+    const dim3 tgrid((unsigned)(p.Np / 64), (unsigned)std::min<long long>(65535, bh - h0));
+    if (d == 128)
+      hipLaunchKernelGGL((vt_fp8_kernel<128>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
+                         p.H, p.kv_len, (int)h0);
+    else
+      hipLaunchKernelGGL((vt_fp8_kernel<64>), tgrid, dim3(256), 0, stream, v, vt, p.N, p.Np,
+                         p.H, p.kv_len, (int)h0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_by_heads(p, (p.N + 255) / 256, 512, [&](dim3 g, const Fp8Params& q) {
+    if (d == 128)
+      hipLaunchKernelGGL((fwd_fp8_kernel<128>), g, dim3(512), 0, stream, q);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<64>), g, dim3(512), 0, stream, q);
+  });
 }
 
 }  // namespace fa

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace fa {
 
 struct FwdParams {
@@ -27,6 +29,7 @@ struct FwdParams {
   uint32_t drop_t;
   float drop_rp;
   uint32_t seed_lo, seed_hi, drop_offset;
+  int bh0, nbh;  // heads of one launch: bh0 .. bh0 + nbh - 1 (set by the launchers)
 };
 
 struct BwdParams {
@@ -52,6 +55,7 @@ struct BwdParams {
   uint32_t drop_t;
   float drop_rp;
   uint32_t seed_lo, seed_hi, drop_offset;
+  int bh0, nbh;  // as in FwdParams
 };
 
 // FP8 forward: Q, K as E4M3 codes [B][H][N][d], V transposed to [B][H][d][Np] (Np = N
@@ -70,7 +74,34 @@ struct Fp8Params {
   float descale_v;
   int causal;
   int wl, wr;       // sliding window as in FwdParams
+  int bh0, nbh;     // as in FwdParams
 };
+
+// A dispatch counts each grid dimension in work-items, in 32 bits. The kernels take a 1-D
+// grid of tiles x heads; a launch of `tiles` workgroups of `threads` work-items per head
+// covers at most this many heads (at least one: a head's tiles times 512 stay below 2^32
+// for every shape the front end accepts), and larger grids go out as several launches
+// over consecutive heads.
+inline int heads_per_launch(long long tiles, int threads) {
+  return (int)std::min<long long>(0xFFFFFFFFLL / (tiles * threads), 0x7FFFFFFFLL);
+}
+
+// Runs go(grid, q) once per group of consecutive heads, q a copy of p with bh0 and nbh set
+// for that group; stops at the first launch error.
+template <typename P, typename G>
+hipError_t launch_by_heads(const P& p, long long tiles, int threads, G&& go) {
+  const long long bh = (long long)p.B * p.H;
+  const int per = heads_per_launch(tiles, threads);
+  P q = p;
+  for (long long h0 = 0; h0 < bh; h0 += per) {
+    q.bh0 = (int)h0;
+    q.nbh = (int)std::min<long long>(per, bh - h0);
+    go(dim3((unsigned)(tiles * q.nbh)), q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 

@@ -20,6 +20,9 @@ Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
      key padding: ``integers(128, 513, size=B)`` (valid length per sequence);
      block mask:  all diagonal blocks kept, plus a uniform draw without replacement
      of off-diagonal blocks until the kept fraction is ``density``.
+
+Inputs of the largest shapes (billions of elements) are drawn on the device instead, by
+``device_normal``: torch's seeded generator, standard normal, directly in the 16-bit type.
 """
 from __future__ import annotations
 
@@ -204,3 +207,28 @@ def custom_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal
         x = (sd * rng.standard_normal(shape)).astype(np.float32)
         out.append(f32_to_f16(x) if dtype == "f16" else f32_to_bf16_bits(x))
     return tuple(out)
+
+
+def device_normal(shape, seed: int, dtype: str = "bf16", count: int = 4,
+                  device: str = "cuda") -> list:
+    """Inputs too large to draw on the host and copy over: ``count`` tensors of standard
+    normal values drawn one after another on the device by one torch generator seeded with
+    ``seed`` (a stream of its own, unrelated to the numpy streams above), drawn directly in
+    bfloat16 or float16. With ``dtype="fp8"`` each is drawn in float32 and quantised per
+    tensor as ``quantize_e4m3`` does; the result is then a list of (uint8 codes, descale)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(count):
+        if dtype == "fp8":
+            x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            amax = float(x.abs().max())
+            descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+            x.div_(np.float32(descale)).clamp_(-448.0, 448.0)
+            out.append((x.to(torch.float8_e4m3fn).view(torch.uint8), descale))
+            del x
+        else:
+            dt = torch.float16 if dtype == "f16" else torch.bfloat16
+            out.append(torch.randn(shape, generator=g, device=device, dtype=dt))
+    return out

@@ -52,6 +52,11 @@
  *   with the extra columns zero-padded: zero columns add nothing to Q K^T, and the padded
  *   output columns are never written. That costs the padded matrix work.
  *   scale must be finite and nonzero (negative values are allowed).
+ *   Sizes: B, H, N >= 1 with B*H*N <= 2^31 - 1 rows and N*d <= 2^31 - 1 elements per
+ *   head; anything larger returns FA_ERR_SHAPE. Every shape within these limits runs: a
+ *   grid holding more work-items than one dispatch counts (2^32 - 1) is enqueued as
+ *   several launches over consecutive heads (the preprocess: over consecutive rows), all
+ *   on the caller's stream.
  *
  * Errors: every entry point validates its arguments on the host before any HIP call and
  * returns a nonzero fa_status without launching anything when they are invalid. A failed

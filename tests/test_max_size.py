@@ -1,0 +1,272 @@
+"""GPU parity at the largest shapes the library accepts.
+
+The front end accepts any shape whose flat row count B*H*N and per-head element count
+N*d both fit in a signed 32-bit int. These tests run at those limits:
+
+  * the longest sequence at d = 128 (N = 2^24 - 1, one head; its last element offset is
+    within 128 of 2^31), bf16 forward + backward and the FP8 forward, under a causal
+    sliding window of 256 keys so that the oracle can check sampled rows from the few
+    keys each one sees;
+  * the most rows (B*H*N = 2^31 - 128 at d = 8): the forward's grid then holds 2^32
+    work-items, one more than a dispatch can count, so it goes out as two launches;
+  * 2^24 + 2^12 heads of three rows, with key padding and, in one case, dropout: every
+    pass of forward and backward is split into launches over consecutive heads, with the
+    splits falling inside batch entries;
+  * the backward preprocess over 2^29 + 2^14 rows (two launches over rows), and the FP8
+    V transpose over 70,007 heads (more than 65,535, the most one launch puts along y).
+
+Inputs are drawn on the device (``inputs.device_normal``); only the rows each check
+needs are copied back. Rows near the ends of every launch are among those checked. With
+the sliding window, the oracle runs on a slice of the head that holds every key the
+checked rows see: a query row's result depends only on the keys it may attend, and the
+window and causal tests depend only on the distance between query and key, which a
+slice keeps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_46_amd as fa
+from exact_io_aware_46_amd import inputs as inp
+from oracle import attention as orc
+from tests.fp8_bound import fp8_bound_rows, rel_l2
+from tests.gpu_util import (O_REL_L2, check_grad, check_lse, check_o, run_fp8, say, to_bits,
+                            to_f64)
+
+pytestmark = pytest.mark.gpu
+
+N_MAX_128 = (2 ** 31 - 1) // 128          # 16,777,215: the longest sequence at d = 128
+DROP_O_SLACK = 2.0 ** -7                  # as in the dropout parity tests
+
+
+def _need(gib):
+    free = torch.cuda.mem_get_info()[0]
+    if free < gib * 2 ** 30:
+        pytest.skip(f"needs {gib} GiB of free device memory, {free / 2 ** 30:.1f} GiB free")
+
+
+def _release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _host(t):
+    """16-bit device rows -> what the oracle reads (bf16 bit patterns or float16)."""
+    return t.cpu().numpy() if t.dtype == torch.float16 else to_bits(t)
+
+
+def _window_centres(N, extra, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = {0, 1, 255, 256, 4095, 2 ** 23, N - 256, N - 255, N - 129, N - 2, N - 1}
+    return sorted(fixed | {int(x) for x in rng.integers(0, N, extra)})
+
+
+def test_longest_sequence_forward_backward_sampled_windows():
+    N, d, W = N_MAX_128, 128, 255
+    scale = float(np.float32(d ** -0.5))
+    _need(40)
+    say(f"[max] bf16 B=1 H=1 N={N} d={d} causal window ({W}, 0): forward + backward")
+    q, k, v, do = inp.device_normal((1, 1, N, d), 4601)
+    o, lse = fa.forward(q, k, v, scale, True, window=(W, 0))
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale, True, window=(W, 0))
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    got = {key: [] for key in ("O", "LSE", "dQ", "dK", "dV")}
+    ref = {key: [] for key in got}
+    for j in _window_centres(N, 9, 4602):
+        # Keys j-W .. j+W: queries j .. j+W see all their keys there, and every query
+        # that sees key j is among them.
+        a, b = max(0, j - W), min(N, j + W + 1)
+        sl = slice(a, b)
+        r = orc.head_backward(*(orc.as_f64(_host(x[0, 0, sl])) for x in (q, k, v, do)),
+                              scale, True, window=(W, 0))
+        rows = slice(j - a, b - a)
+        krows = slice(j - a, (b if b == N else j + 1) - a)
+        got["O"].append(to_f64(o[0, 0, j:b]))
+        got["LSE"].append(to_f64(lse[0, 0, j:b]))
+        got["dQ"].append(to_f64(dq[0, 0, j:b]))
+        got["dK"].append(to_f64(dk[0, 0, a:b])[krows])
+        got["dV"].append(to_f64(dv[0, 0, a:b])[krows])
+        for key in ("O", "LSE", "dQ"):
+            ref[key].append(r[key][rows])
+        for key in ("dK", "dV"):
+            ref[key].append(r[key][krows])
+    cat = {key: (np.concatenate(got[key]), np.concatenate(ref[key])) for key in got}
+    say(f"   rows checked: O/LSE/dQ {cat['O'][0].shape[0]}, dK/dV {cat['dK'][0].shape[0]}")
+    check_o(*cat["O"], "longest sequence")
+    check_lse(*cat["LSE"], "longest sequence")
+    for g in ("dQ", "dK", "dV"):
+        check_grad(*cat[g], g, "longest sequence")
+    del q, k, v, do, o, lse, dq, dk, dv
+    _release()
+
+
+def test_fp8_longest_sequence_sampled_rows():
+    N, d, W = N_MAX_128, 128, 255
+    scale = float(np.float32(d ** -0.5))
+    _need(24)
+    say(f"[max] fp8 B=1 H=1 N={N} d={d} causal window ({W}, 0)")
+    (q8, dsq), (k8, dsk), (v8, dsv) = inp.device_normal((1, 1, N, d), 4603, "fp8", 3)
+    desc = (dsq, dsk, dsv)
+    o, lse = fa.forward_fp8(q8, k8, v8, scale, desc, True, window=(W, 0))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = _window_centres(N, 13, 4604)
+    O, R, L, LR, worst = [], [], [], [], 0.0
+    for i in rows:
+        a = max(0, i - W)
+        Q8, K8, V8 = (x[0, 0, a:i + 1].cpu().numpy() for x in (q8, k8, v8))
+        r = [i - a]
+        o_ref, l_ref = orc.head_forward_fp8(Q8, K8, V8, desc, scale, True, rows=r,
+                                            window=(W, 0))
+        bound = fp8_bound_rows(Q8[r], K8, V8, desc, scale, o_ref,
+                               orc.allowed(r, i + 1 - a, True, None, None, (W, 0)))[0]
+        og = to_f64(o[0, 0, i])
+        err = np.abs(og - o_ref[0])
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), f"fp8 longest sequence row {i}: {err.max():.3e}"
+        O.append(og)
+        R.append(o_ref[0])
+        L.append(float(lse[0, 0, i]))
+        LR.append(l_ref[0])
+    check_lse(np.array(L), np.array(LR), "fp8 longest sequence")
+    rl = rel_l2(np.array(O), np.array(R))
+    say(f"   {len(rows)} rows: max err/bound {worst:.3f}, rel-L2 {rl:.3e}")
+    assert rl <= O_REL_L2
+    del q8, k8, v8, o, lse
+    _release()
+
+
+def test_most_rows_forward_runs_as_two_launches():
+    B, H, N, d, W = 1, 128, N_MAX_128, 8, 15   # B*H*N = 2^31 - 128
+    scale = float(np.float32(d ** -0.5))
+    _need(160)
+    say(f"[max] bf16 forward B={B} H={H} N={N} d={d} (B*H*N = {B * H * N}) causal window "
+        f"({W}, 0)")
+    q, k, v = inp.device_normal((B, H, N, d), 4605, count=3)
+    o, lse = fa.forward(q, k, v, scale, True, window=(W, 0))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.Generator(np.random.PCG64(4606))
+    # Eight-wave workgroups of 256 queries: 65,536 per head, 2^25 work-items per head, so
+    # the first launch holds heads 0 .. 126 and the second head 127.
+    sel = sorted({(h, i) for h in (0, 1, 126, 127) for i in (0, 15, 16, N - 1)} |
+                 {(int(rng.integers(H)), int(rng.integers(N))) for _ in range(24)})
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for h, i in sel:
+        a = max(0, i - W)
+        o_ref, l_ref = orc.head_forward(*(orc.as_f64(to_bits(x[0, h, a:i + 1]))
+                                          for x in (q, k, v)),
+                                        scale, True, rows=[i - a], window=(W, 0))
+        got_o.append(to_f64(o[0, h, i]))
+        ref_o.append(o_ref[0])
+        got_l.append(float(lse[0, h, i]))
+        ref_l.append(l_ref[0])
+    say(f"   {len(sel)} rows checked")
+    check_o(np.array(got_o), np.array(ref_o), "most rows")
+    check_lse(np.array(got_l), np.array(ref_l), "most rows")
+    del q, k, v, o, lse
+    _release()
+
+
+@pytest.mark.parametrize("case", ["bf16", "f16_dropout_causal"])
+def test_heads_split_over_launches(case):
+    B, H, N, d = 4097, 4096, 3, 8                  # 2^24 + 2^12 heads
+    BH = B * H
+    dtype = "f16" if case.startswith("f16") else "bf16"
+    causal = "causal" in case
+    drop = (0.3, 77_000_001, 5) if "dropout" in case else None
+    scale = float(np.float32(d ** -0.5))
+    _need(12)
+    say(f"[max] {case}: B={B} H={H} N={N} d={d} with key padding, forward + backward")
+    q, k, v, do = inp.device_normal((B, H, N, d), 4607 + causal, dtype)
+    kv = np.random.Generator(np.random.PCG64(4609)).integers(0, N + 1, B).astype(np.int32)
+    kv_d = torch.from_numpy(kv).cuda()
+    o, lse = fa.forward(q, k, v, scale, causal, None, kv_d, dropout=drop)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale, causal, None, kv_d, dropout=drop)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    # Launch limits: 2^23 - 1 heads for 512-thread workgroups (forward, dQ, and dK/dV with
+    # dropout), 2^24 - 1 for the 256-thread dK/dV workgroups.
+    p8, p4 = 2 ** 23 - 1, 2 ** 24 - 1
+    edges = {0, 1, p8 - 1, p8, p8 + 1, 2 * p8 - 1, 2 * p8, 2 * p8 + 1, p4 - 1, p4, p4 + 1,
+             BH - 2, BH - 1}
+    rng = np.random.Generator(np.random.PCG64(4610))
+    sel = sorted(edges | {int(x) for x in rng.integers(0, BH, 40)})
+    empty = [bh for bh in sel if kv[bh // H] == 0]
+    say(f"   {len(sel)} heads checked ({len(empty)} with no valid key)")
+    got = {key: [] for key in ("O", "LSE", "dQ", "dK", "dV")}
+    ref = {key: [] for key in got}
+    for bh in sel:
+        b, h = divmod(bh, H)
+        hd = None if drop is None else (*drop, bh)
+        r = orc.head_backward(*(orc.as_f64(_host(x[b, h])) for x in (q, k, v, do)), scale,
+                              causal, None, int(kv[b]), dropout=hd)
+        for key, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+            got[key].append(to_f64(t[b, h]))
+            ref[key].append(r[key])
+    cat = {key: (np.concatenate(got[key]), np.concatenate(ref[key])) for key in got}
+    check_o(*cat["O"], case, DROP_O_SLACK if drop else 0.0)
+    check_lse(*cat["LSE"], case)
+    for g in ("dQ", "dK", "dV"):
+        check_grad(*cat[g], g, case)
+    del q, k, v, do, o, lse, dq, dk, dv
+    _release()
+
+
+def test_preprocess_rows_split_over_launches():
+    B, H, N, d = 1, 32, 2 ** 24 + 512, 8        # 2^29 + 2^14 rows
+    rows = B * H * N
+    _need(20)
+    say(f"[max] preprocess over {rows} rows at d={d}")
+    o, do = inp.device_normal((B, H, N, d), 4611, count=2)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa_bwd_preprocess(o, do, delta, B, H, N, d)
+    torch.cuda.synchronize()
+    per = (2 ** 32 - 1) // 256 * 32                 # rows of one launch at 8 threads a row
+    assert per < rows
+    rng = np.random.Generator(np.random.PCG64(4612))
+    sel = np.array(sorted({0, per - 1, per, per + 1, rows - 1} |
+                          {int(x) for x in rng.integers(0, rows, 40)}))
+    of, gf, df = o.view(rows, d), do.view(rows, d), delta.view(rows)
+    idx = torch.from_numpy(sel).cuda()
+    ref = orc.delta(to_bits(of[idx]), to_bits(gf[idx]))
+    np.testing.assert_allclose(df[idx].cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+    del o, do, delta
+    _release()
+
+
+def test_fp8_transpose_over_more_heads_than_one_launch():
+    B, H, N, d = 7, 10001, 5, 64                # 70,007 heads
+    rng = np.random.Generator(np.random.PCG64(4613))
+    q8, dsq = inp.quantize_e4m3(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    k8, dsk = inp.quantize_e4m3(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    v8, dsv = inp.quantize_e4m3(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    kv = rng.integers(0, N + 1, B).astype(np.int32)
+    desc, scale = (dsq, dsk, dsv), float(np.float32(d ** -0.5))
+    say(f"[max] fp8 B={B} H={H} N={N} d={d} with key padding")
+    O, L, ws = run_fp8(q8, k8, v8, scale, desc, False, None, kv)
+    vt = ws.cpu().numpy().reshape(B, H, d, 128)
+    sel = sorted({0, 65534, 65535, 65536, B * H - 1} |
+                 {int(x) for x in rng.integers(0, B * H, 30)})
+    o_got, o_ref, worst = [], [], 0.0
+    for bh in sel:
+        b, h = divmod(bh, H)
+        n = int(kv[b])
+        assert np.array_equal(vt[b, h, :, :n], v8[b, h, :n].T), bh
+        assert (vt[b, h, :, n:] == 0).all(), bh
+        r_o, r_l = orc.head_forward_fp8(q8[b, h], k8[b, h], v8[b, h], desc, scale, False,
+                                        None, n)
+        bound = fp8_bound_rows(q8[b, h], k8[b, h], v8[b, h], desc, scale, r_o,
+                               orc.allowed(np.arange(N), N, False, None, n))
+        err = np.abs(O[b, h] - r_o)
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), bh
+        check_lse(L[b, h], r_l, f"fp8 head {bh}")
+        o_got.append(O[b, h])
+        o_ref.append(r_o)
+    rl = rel_l2(np.concatenate(o_got), np.concatenate(o_ref))
+    say(f"   {len(sel)} heads: max err/bound {worst:.3f}, rel-L2 {rl:.3e}")
+    assert rl <= O_REL_L2
