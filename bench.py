@@ -400,14 +400,17 @@ def footprint_sweep(torch, base, steps=10, warmup=3):
 
 
 KERNEL_SOURCES = {"fwd_kernel": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.h"],
-                  "bwd_kernel": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.h"],
+                  "bwd_kernel": ["fa_bwd.hip", "fa_bwd_rk.hip", "fa_bwd_rk_drop.hip", "fa_device.hpp",
+                                 "fa_internal.h"],
                   "fp8_kernel": ["fa_fwd_fp8.hip", "fa_device.hpp", "fa_internal.h"]}
 
 
 def source_hash(kind):
     """Hash of a kernel's sources with // comments, trailing blanks and empty lines left
-    out, so an edit of comments alone keeps the recorded counters."""
+    out, so an edit of comments alone keeps the recorded counters; a source built with
+    options of its own adds them."""
     import hashlib
+    from exact_io_aware_46_amd import build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "exact_io_aware_46_amd", "csrc", f)) as fh:
@@ -415,6 +418,8 @@ def source_hash(kind):
                 code = line.split("//", 1)[0].rstrip()
                 if code:
                     h.update(code.encode() + b"\n")
+        if f in build.SOURCE_FLAGS:
+            h.update(" ".join(build.SOURCE_FLAGS[f]).encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -18,18 +18,24 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 PEAK_LIB = os.path.join(PKG, "libmfma_peak.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_rk.hip", "fa_bwd_rk_drop.hip",
+           "fa_fwd_fp8.hip", "fa_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the device compiler from forming packed fp32 instructions.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Options for one source only: the one-wave dK/dV kernel's instances without dropout form
+# their matrix products in VGPRs (the compiler otherwise keeps S and dP in accumulation
+# registers and copies each element out before the elementwise work).
+SOURCE_FLAGS = {"fa_bwd_rk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

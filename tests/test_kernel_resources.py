@@ -15,11 +15,12 @@ import pytest
 
 from exact_io_aware_46_amd import build as fabuild
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_bwd_rk.hip", "fa_bwd_rk_drop.hip", "fa_fwd_fp8.hip"]
 
 
 def _report(src):
-    cmd = [fabuild.HIPCC, *[f for f in fabuild.CFLAGS if f != "-fPIC"], "-x", "hip",
+    cmd = [fabuild.HIPCC, *[f for f in fabuild.CFLAGS if f != "-fPIC"],
+           *fabuild.SOURCE_FLAGS.get(src, []), "-x", "hip",
            "--cuda-device-only", "-c", os.path.join(fabuild.CSRC, src), "-o", os.devnull,
            "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
