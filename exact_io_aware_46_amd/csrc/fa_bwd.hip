@@ -573,6 +573,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 2 : 1))) void bwd_dq_ker
 #pragma unroll
   for (int j = 0; j < DB; ++j) acc[j] = zero16();
 
+  f32x16 ndv;  // -D in every element: the start of each block's dP product
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndv[i] = ndq;
+
   // Lane offsets of the operand loads (see the dK/dV pass): K and V rows as the A operand
   // (step st: XOR (st << 5)), and the K^T transpose loads (column block j: XOR (j << 6)).
   const int a_off = swz_off<CH>(perm_row(l32), 8 * hi);
@@ -589,10 +593,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 2 : 1))) void bwd_dq_ker
   auto tile = [&](auto masked, int k0, const char* sK, const char* sV, bool need_mask)
                   __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    // One 32-key block at a time, so only one block of S and dP is live.
+    // One 32-key block at a time, so only one block of S and dP is live. Without dropout
+    // the dP product starts from -D (every element of a lane is the lane's query), so the
+    // matrix unit returns dP - D; with dropout dP must be masked and scaled first.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s = zero16(), dp = DROP ? zero16() : ndv;
       const int kbo = kb * 32 * ROWB;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -628,7 +634,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && NW == 4 ? 2 : 1))) void bwd_dq_ker
           const bool keep = drop_keep(kwd[i >> 1], i & 1, p.drop_t, thi);
           dp[i] = pv * ((keep ? dp[i] * p.drop_rp : 0.f) + ndq);  // dS = P (dP - D)
         } else {
-          dp[i] = pv * (dp[i] + ndq);
+          dp[i] = pv * dp[i];
         }
       }
 #pragma unroll
