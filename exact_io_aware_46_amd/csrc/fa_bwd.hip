@@ -19,7 +19,8 @@
 //
 // gfx950 mapping shared by both passes: 8 waves per workgroup (two per SIMD; 4 at d = 256,
 // where the accumulators need one wave per SIMD, and 4 in the dK/dV pass on the 128-wide
-// layout, which keeps K and V in registers), each owning 32 rows of the outer dimension;
+// layout, which keeps K and V in registers: that kernel is in fa_bwd_rk.hip), each owning
+// 32 rows of the outer dimension;
 // inner tiles are copied HBM -> LDS by buffer loads into LDS (no registers),
 // double-buffered, row-major with XOR-swizzled 16-byte chunks; operands that must be
 // contraction-major are read with LDS transpose loads.
