@@ -9,9 +9,10 @@ N*d both fit in a signed 32-bit int. These tests run at those limits:
     keys each one sees;
   * the most rows (B*H*N = 2^31 - 128 at d = 8): the forward's grid then holds 2^32
     work-items, one more than a dispatch can count, so it goes out as two launches;
-  * 2^24 + 2^12 heads of three rows, with key padding and, in one case, dropout: every
-    pass of forward and backward is split into launches over consecutive heads, with the
-    splits falling inside batch entries;
+  * 2^24 + 2^12 heads of two or three rows at d = 8, 128 and 256, with key padding and,
+    in two cases, dropout: every pass of forward and backward, in every kernel family, is
+    split into launches over consecutive heads, with the splits falling inside batch
+    entries;
   * the backward preprocess over 2^29 + 2^14 rows (two launches over rows), and the FP8
     V transpose over 70,007 heads (more than 65,535, the most one launch puts along y).
 
@@ -170,15 +171,23 @@ def test_most_rows_forward_runs_as_two_launches():
     _release()
 
 
-@pytest.mark.parametrize("case", ["bf16", "f16_dropout_causal"])
-def test_heads_split_over_launches(case):
-    B, H, N, d = 4097, 4096, 3, 8                  # 2^24 + 2^12 heads
+@pytest.mark.parametrize("case,d,N,gib", [
+    ("bf16", 8, 3, 12),
+    ("f16_dropout_causal", 8, 3, 12),
+    ("bf16_causal", 128, 2, 80),
+    ("f16_dropout_causal", 128, 2, 80),
+    ("bf16_causal", 256, 2, 160),
+])
+def test_heads_split_over_launches(case, d, N, gib):
+    """Every kernel family (the 64-, 128- and 256-wide layouts; forward, dQ and both dK/dV
+    kernels, with and without dropout) over 2^24 + 2^12 heads of two or three rows."""
+    B, H = 4097, 4096                              # 2^24 + 2^12 heads
     BH = B * H
     dtype = "f16" if case.startswith("f16") else "bf16"
     causal = "causal" in case
     drop = (0.3, 77_000_001, 5) if "dropout" in case else None
     scale = float(np.float32(d ** -0.5))
-    _need(12)
+    _need(gib)
     say(f"[max] {case}: B={B} H={H} N={N} d={d} with key padding, forward + backward")
     q, k, v, do = inp.device_normal((B, H, N, d), 4607 + causal, dtype)
     kv = np.random.Generator(np.random.PCG64(4609)).integers(0, N + 1, B).astype(np.int32)
@@ -188,8 +197,9 @@ def test_heads_split_over_launches(case):
     torch.cuda.synchronize()
     for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         assert bool(torch.isfinite(t).all()), name
-    # Launch limits: 2^23 - 1 heads for 512-thread workgroups (forward, dQ, and dK/dV with
-    # dropout), 2^24 - 1 for the 256-thread dK/dV workgroups.
+    # One tile per head in every pass. Launch limits: 2^23 - 1 heads for 512-thread
+    # workgroups (eight waves: forward and dQ up to d = 128, the two-wave dK/dV kernel),
+    # 2^24 - 1 for 256-thread ones (the one-wave dK/dV kernel, every kernel at d = 256).
     p8, p4 = 2 ** 23 - 1, 2 ** 24 - 1
     edges = {0, 1, p8 - 1, p8, p8 + 1, 2 * p8 - 1, 2 * p8, 2 * p8 + 1, p4 - 1, p4, p4 + 1,
              BH - 2, BH - 1}
