@@ -293,7 +293,11 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = 2 * kh + (w >> 2), i0 = 4 * (w & 3);
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], 0, false);
+        // The first conversion fills the low half-word; the second overwrites the high one,
+        // so the first's pass-through operand can be any live register (here the bits of
+        // an input, dead after this) instead of a zero materialised per word.
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1],
+                                                __float_as_int(s[kb][i0]), false);
         x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0 + 2], s[kb][i0 + 3], x, true);
         pf[w] = x;
       }
