@@ -77,6 +77,16 @@ def test_fwd_bad_shape(lib, B, H, N):
     assert fwd(lib, B=B, H=H, N=N) == 2
 
 
+# The size limits: B*H*N rows and N*d elements per head each at most 2^31 - 1.
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1 << 24, 128),        # N*d = 2^31
+                                     (1, 1, 1 << 23, 256),        # N*d = 2^31
+                                     (1 << 7, 1 << 7, 1 << 17, 8),  # B*H*N = 2^31
+                                     (3, 5, 143165577, 8)])       # B*H*N = 2^31 + 7
+def test_sizes_one_past_the_limits_are_rejected(lib, B, H, N, d):
+    assert fwd(lib, B=B, H=H, N=N, d=d) == 2
+    assert lib.fa_bwd_workspace_bytes(B, H, N, d) == 0
+
+
 # Supported: multiples of 8 from 8 to 256.
 @pytest.mark.parametrize("d", [0, 4, 20, 100, 260, 264, 512, -64])
 def test_fwd_unsupported_head_dim(lib, d):
