@@ -92,6 +92,7 @@ template <typename P, typename G>
 hipError_t launch_by_heads(const P& p, long long tiles, int threads, G&& go) {
   const long long bh = (long long)p.B * p.H;
   const int per = heads_per_launch(tiles, threads);
+  if (per < 1) return hipErrorInvalidConfiguration;  // one head alone too large (not reached)
   P q = p;
   for (long long h0 = 0; h0 < bh; h0 += per) {
     q.bh0 = (int)h0;
