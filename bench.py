@@ -531,9 +531,9 @@ def cpu_baseline(x, heads=4):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in the design notes, not implemented.",
-              file=sys.stderr)
+        print(f"bench.py: libfa is measured on one GPU only (asked for --gpus {args.gpus}); "
+              "how the path would shard over several GPUs is described in the design notes, "
+              "not implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
     from exact_io_aware_46_amd import inputs as inp
