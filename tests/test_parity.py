@@ -573,6 +573,20 @@ def test_other_head_dims(d, N, causal, window, kv, bm):
                   what=f"head dim {d}", window=window)
 
 
+_TESTED_DIMS = {8, 24, 32, 40, 64, 72, 96, 120, 128, 200, 256}
+
+
+@pytest.mark.parametrize("d", [d for d in range(8, 257, 8) if d not in _TESTED_DIMS])
+def test_every_other_head_dim(d):
+    """Every supported head dim not covered above (multiples of 8 up to 256), each on the
+    padded tiles of its layout: 130 queries (ragged against every tile), causal with key
+    padding on two batch entries, forward and backward against the oracle."""
+    q, k, v, do = inp.custom_inputs(2, 2, 130, d, seed=5000 + d)
+    kvn = np.array([130, 77], dtype=np.int32)
+    run_and_check(q, k, v, do, float(np.float32(d ** -0.5)), True, None, kvn,
+                  what=f"head dim {d}")
+
+
 @pytest.mark.parametrize("d", [24, 96])
 def test_other_head_dims_f16_and_dropout(d):
     N = 257
