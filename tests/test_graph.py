@@ -56,3 +56,43 @@ def test_captured_forward_backward_replays_equal_eager(d, kv):
         for a, b in zip((o, lse, dq, dk, dv), ref):
             it = torch.int16 if a.element_size() == 2 else torch.int32
             assert torch.equal(a.view(it), b.view(it)), f"replay {r} differs"
+
+
+def test_calls_on_two_streams_at_once_equal_sequential_calls():
+    """The library keeps no state between calls: forward + backward of two problems of
+    different shapes, each on its own stream (default priority) and running at the same
+    time, equal the same calls made one after another, bit for bit."""
+    probs = []
+    for i, (N, d) in enumerate([(700, 128), (900, 64)]):
+        q, k, v, do = (to_dev(x) for x in inp.custom_inputs(1, 4, N, d, seed=331 + i))
+        probs.append((q, k, v, do, float(np.float32(d ** -0.5))))
+
+    def run(pr, stream=None):
+        q, k, v, do, sc = pr
+        o, lse = fa.forward(q, k, v, sc, True, stream=stream)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(*q.shape), dtype=torch.uint8,
+                         device="cuda")
+        dq, dk, dv = fa.backward(q, k, v, o, lse, do, sc, True, workspace=ws, stream=stream)
+        return o, lse, dq, dk, dv
+
+    say("[streams] sequential reference")
+    ref = [run(pr) for pr in probs]
+    torch.cuda.synchronize()
+    say("[streams] two streams at once")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        cur = []
+        for pr, s in zip(probs, streams):
+            with torch.cuda.stream(s):
+                cur.append(run(pr, stream=s))
+        outs.append(cur)
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for cur in outs:
+        for got, want in zip(cur, ref):
+            for a, b in zip(got, want):
+                assert torch.equal(a.view(torch.int8), b.view(torch.int8))
